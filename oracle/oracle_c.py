@@ -1,0 +1,142 @@
+"""ctypes front-end of the fp64 C oracle (``ssm_oracle.c``).
+
+Test infrastructure only: tests, the smoke check and bench.py's CPU-baseline
+leg call it; the HIP path never does.  Inputs may be numpy arrays or CPU torch
+tensors of any float dtype; they are upcast exactly to fp64.  Outputs are fp64
+numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+# ORACLE_LIB_OVERRIDE points the loader at another build (used to check that
+# the pins fail on deliberately broken copies of the oracle).
+_LIB_PATH = os.environ.get("ORACLE_LIB_OVERRIDE") or os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (fp64, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                               "-fno-fast-math", "-Wall", "-o", tmp, _SRC, "-lm", "-lpthread"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.environ.get("ORACLE_LIB_OVERRIDE") and (not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I = ctypes.c_int64
+        lib.oracle_scan_fwd.argtypes = [I, I, I, I] + [P] * 8 + [ctypes.c_int, P, P, P, I, P,
+                                                                ctypes.c_int]
+        lib.oracle_scan_fwd.restype = ctypes.c_int
+        lib.oracle_scan_bwd.argtypes = [I, I, I, I] + [P] * 8 + [ctypes.c_int, P, P, P] + [P] * 9 \
+            + [ctypes.c_int]
+        lib.oracle_scan_bwd.restype = ctypes.c_int
+        lib.oracle_state_update.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, ctypes.c_int, P]
+        lib.oracle_state_update.restype = ctypes.c_int
+        for f in ("oracle_softplus", "oracle_sigmoid", "oracle_silu"):
+            getattr(lib, f).argtypes = [ctypes.c_double]
+            getattr(lib, f).restype = ctypes.c_double
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor
+        import torch
+        x = x.detach().to("cpu", torch.float64).contiguous().numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, h0=None,
+             chunk_len=None, nthreads=None):
+    """Returns (y, h_final, chunk_states or None) in fp64."""
+    u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
+    D, z, delta_bias, h0 = map(_f64, (D, z, delta_bias, h0))
+    Bsz, L, Dm = u.shape
+    N = A.shape[1]
+    y = np.empty((Bsz, L, Dm))
+    hf = np.empty((Bsz, Dm, N))
+    cs = None
+    if chunk_len:
+        K = (L + chunk_len - 1) // chunk_len
+        cs = np.empty((Bsz, K, Dm, N))
+    rc = _load().oracle_scan_fwd(Bsz, L, Dm, N, _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D),
+                                 _p(z), _p(delta_bias), int(bool(delta_softplus)), _p(h0), _p(y),
+                                 _p(hf), int(chunk_len or 0), _p(cs),
+                                 int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"oracle_scan_fwd failed ({rc})")
+    return y, hf, cs
+
+
+def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, h0=None,
+             dy=None, dh_final=None, nthreads=None):
+    """Returns a dict of fp64 gradients: du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0."""
+    u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
+    D, z, delta_bias, h0, dy, dh_final = map(_f64, (D, z, delta_bias, h0, dy, dh_final))
+    Bsz, L, Dm = u.shape
+    N = A.shape[1]
+    out = dict(du=np.empty_like(u), ddelta=np.empty_like(u), dA=np.empty((Dm, N)),
+               dB=np.empty((Bsz, L, N)), dC=np.empty((Bsz, L, N)),
+               dD=np.empty(Dm) if D is not None else None,
+               dz=np.empty_like(u) if z is not None else None,
+               ddelta_bias=np.empty(Dm) if delta_bias is not None else None,
+               dh0=np.empty((Bsz, Dm, N)))
+    rc = _load().oracle_scan_bwd(Bsz, L, Dm, N, _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z),
+                                 _p(delta_bias), int(bool(delta_softplus)), _p(h0), _p(dy),
+                                 _p(dh_final), _p(out["du"]), _p(out["ddelta"]), _p(out["dA"]),
+                                 _p(out["dB"]), _p(out["dC"]), _p(out["dD"]), _p(out["dz"]),
+                                 _p(out["ddelta_bias"]), _p(out["dh0"]),
+                                 int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"oracle_scan_bwd failed ({rc})")
+    return out
+
+
+def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True):
+    """One decode step. Returns (new_state, y) in fp64; the input is not modified."""
+    st = _f64(state).copy()
+    u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
+    D, z, delta_bias = map(_f64, (D, z, delta_bias))
+    Bsz, Dm, N = st.shape
+    y = np.empty((Bsz, Dm))
+    rc = _load().oracle_state_update(Bsz, Dm, N, _p(st), _p(u), _p(delta), _p(A), _p(B), _p(C),
+                                     _p(D), _p(z), _p(delta_bias), int(bool(delta_softplus)), _p(y))
+    if rc != 0:
+        raise ValueError(f"oracle_state_update failed ({rc})")
+    return st, y
+
+
+def softplus(x: float) -> float:
+    return _load().oracle_softplus(float(x))
+
+
+def silu(x: float) -> float:
+    return _load().oracle_silu(float(x))

@@ -1,0 +1,240 @@
+"""Benchmark of the selective-SSM scan on one MI355X.
+
+Default: the forward scan at the Mamba-370m layer shape (batch 8, length 2048,
+2048 channels, 16 states, fp32, outputs y and the final state).  One step is
+one forward pass over one batch of synthetic inputs already resident in HBM;
+three input sets are rotated so that the 256 MB last-level cache cannot hold a
+step's inputs.  Prints ONE JSON line (rank 0).
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+``--workload`` also accepts the other shapes (mamba-2.8b-layer-fwd,
+decode-state-update, million-length-fwd, million-length-bwd); their lines use
+the same keys and are for reference, the default workload is the headline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "selective-scan fwd tokens·channels/s and HBM GB/s (% of peak), Mamba-370m shape"
+UNIT = "tokens*channels/s"
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba-370m-layer-fwd",
+                    choices=["mamba-370m-layer-fwd", "mamba-2.8b-layer-fwd", "decode-state-update",
+                             "million-length-fwd", "million-length-bwd"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=3, help="input sets rotated between steps")
+    return ap.parse_args()
+
+
+def _source_sha(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "selective_state_space_10_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key: str, sha: str, launches_per_step: int = 1):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def _time_launches(fn, steps, warmup, rotate_inputs):
+    """Per-launch HIP-event durations on the launch stream, plus the wall time
+    of the whole timed region (both synchronised on both sides)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(rotate_inputs[i % len(rotate_inputs)])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn(rotate_inputs[i % len(rotate_inputs)])
+        ev[i][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in ev]
+    return start.elapsed_time(stop) / steps, sum(per) / len(per), wall
+
+
+def _cpu_baseline_fwd(p_cpu, sample_desc):
+    from oracle import oracle_c
+    threads = oracle_c.default_threads()
+    kw = {k: p_cpu[k] for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
+    import numpy as np  # noqa: F401
+    conv = {k: oracle_c._f64(v) for k, v in kw.items()}
+    t0 = time.perf_counter()
+    oracle_c.scan_fwd(**conv, delta_softplus=True, nthreads=threads)
+    dt = time.perf_counter() - t0
+    Bsz, L, D = p_cpu["u"].shape
+    return {"value": Bsz * L * D / dt, "unit": UNIT, "cores": threads, "kind": "oracle",
+            "sample": sample_desc, "seconds": round(dt, 3)}
+
+
+def bench_fwd(args, idx, name):
+    import torch
+
+    import selective_state_space_10_amd as m
+    from workloads import WORKLOADS, algorithmic_bytes_fwd, workload_inputs
+    w = WORKLOADS[idx]
+    want_hf = "h_final" in w.outputs
+    sets = [workload_inputs(idx, device="cuda", seed=idx + 100 * r) for r in range(args.rotate)]
+    torch.cuda.synchronize()
+
+    def step(p):
+        m.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["delta_bias"],
+                   True, None, return_final_state=want_hf)
+
+    ms_step, ms_launch, wall = _time_launches(step, args.steps, args.warmup, sets)
+    Bsz, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
+    io_bytes = 4 if w.io_dtype == torch.float32 else 2
+    nbytes = algorithmic_bytes_fwd(Bsz, L, D, N, io_bytes, h_final=want_hf)
+    achieved = nbytes / (ms_launch * 1e-3) / 1e9
+    sha = _source_sha("scan_fwd.hip", "device_common.hpp", "kernels.hpp")
+    traffic = _traffic(f"fwd:{name}", sha)
+    line = {
+        "metric": METRIC if idx == 1 else f"selective-scan fwd tokens*channels/s, {name}",
+        "value": Bsz * L * D / (ms_step * 1e-3),
+        "unit": UNIT, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if io_bytes == 4 else "bf16 storage, f32 compute",
+        "data": "synthetic (seeded Gaussian inputs of the layer's shape, rotated over "
+                f"{args.rotate} resident sets)",
+        "config": {"workload": name, "batch": Bsz, "seqlen": L, "dim": D, "dstate": N,
+                   "io_dtype": str(w.io_dtype).replace("torch.", ""), "outputs": list(w.outputs),
+                   "gpu": torch.cuda.get_device_name(), "wall_s": round(wall, 4)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes": nbytes,
+                     "kernel_ms": ms_launch, "source_sha": sha},
+    }
+    if not args.no_cpu_baseline and idx == 1:
+        pc = workload_inputs(idx, device="cuda", seed=idx)
+        pc = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in pc.items()}
+        line["cpu_baseline"] = _cpu_baseline_fwd(
+            pc, f"one full step ({Bsz}x{L}x{D}x{N}) of the fp64 C oracle, forward")
+    return line
+
+
+def bench_decode(args):
+    import torch
+
+    import selective_state_space_10_amd as m
+    from workloads import WORKLOADS, algorithmic_bytes_decode, decode_inputs
+    w = WORKLOADS[3]
+    d = decode_inputs(w.batch, w.dim, w.dstate, w.steps, w.io_dtype, seed=3, device="cuda")
+    states = [d["state"].clone() for _ in range(4)]  # rotated so the state is not cache-resident
+    tok = list(range(w.steps))
+
+    def step(t):
+        st = states[t % len(states)]
+        m.state_update(st, d["u"][t], d["delta"][t], d["A"], d["B"][t], d["C"][t], d["D"],
+                       d["z"][t], d["delta_bias"], True)
+
+    ms_step, ms_launch, wall = _time_launches(step, args.steps, args.warmup, tok)
+    nbytes = algorithmic_bytes_decode(w.batch, w.dim, w.dstate, 2)
+    achieved = nbytes / (ms_launch * 1e-3) / 1e9
+    return {"metric": "decode state update tokens*channels/s", "unit": UNIT,
+            "value": w.batch * w.dim / (ms_step * 1e-3), "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16 storage, f32 compute",
+            "data": "synthetic", "config": {"workload": "decode-state-update", "batch": w.batch,
+                                            "dim": w.dim, "dstate": w.dstate},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "algorithmic_bytes": nbytes, "kernel_ms": ms_launch}}
+
+
+def bench_bwd(args):
+    import torch
+
+    import selective_state_space_10_amd as m
+    from workloads import WORKLOADS, cotangent, workload_inputs
+    w = WORKLOADS[4]
+    p = workload_inputs(4, device="cuda")
+    y, _, cs = m.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                          p["delta_bias"], True, None, save_chunk_states=True)
+    dy = cotangent(y, 4)
+    del y
+
+    def step(_):
+        m.scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["delta_bias"],
+                   True, None, cs, dy)
+
+    ms_step, ms_launch, wall = _time_launches(step, args.steps, args.warmup, [0])
+    Bsz, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
+    nbytes = (4 * Bsz * L * D * 2 + 3 * Bsz * L * D * 2 + 4 * Bsz * L * N * 2 + cs.numel() * 4
+              + D * N * 4 * 2 + D * 4 * 4)
+    achieved = nbytes / (ms_launch * 1e-3) / 1e9
+    return {"metric": "selective-scan bwd tokens*channels/s, million-length", "unit": UNIT,
+            "value": Bsz * L * D / (ms_step * 1e-3), "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16 storage, f32 compute",
+            "data": "synthetic", "config": {"workload": "million-length-bwd", "batch": Bsz,
+                                            "seqlen": L, "dim": D, "dstate": N},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "algorithmic_bytes": nbytes, "kernel_ms": ms_launch}}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import selective_state_space_10_amd as m
+    m.load()
+    if args.workload == "mamba-370m-layer-fwd":
+        line = bench_fwd(args, 1, args.workload)
+    elif args.workload == "mamba-2.8b-layer-fwd":
+        line = bench_fwd(args, 2, args.workload)
+    elif args.workload == "million-length-fwd":
+        args.rotate = 1
+        line = bench_fwd(args, 4, args.workload)
+    elif args.workload == "decode-state-update":
+        line = bench_decode(args)
+    else:
+        line = bench_bwd(args)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+/*
+ * ssm_scan.h -- C ABI of the selective-SSM scan library for AMD MI355X (gfx950).
+ *
+ * The library computes the selective state-space scan of Mamba (Gu & Dao,
+ * "Mamba: Linear-Time Sequence Modeling with Selective State Spaces", arXiv
+ * 2312.00752).  The pages this follows are the paper's reading guide on
+ * xyznot.com and the mamba-minimal news page on ja.news.hada.io:
+ *
+ *   per batch row b, channel d and state index n, for t = 0 .. L-1
+ *     s_t       = delta[b,t,d] + delta_bias[d]
+ *     dt_t      = softplus(s_t) if delta_softplus else s_t
+ *                 (reading guide, "Seçim Mekanizması (S6)": the step size is
+ *                 softplus of a parameter plus an input-dependent term)
+ *     dA        = exp(dt_t * A[d,n])       (zero-order hold of A, "Yöntem")
+ *     dBu       = dt_t * B[b,t,n] * u[b,t,d]
+ *                 (the deltaB_u term of the sequential loop quoted on the
+ *                 mamba-minimal page; first-order form of the ZOH input term)
+ *     h[n]      = dA * h[n] + dBu          (discrete recurrence, "Yöntem")
+ *     y[b,t,d]  = (sum_n C[b,t,n] * h[n] + D[d] * u[b,t,d]) * silu(z[b,t,d])
+ *                 (output y = C h, "Yöntem"; D skip and the multiplicative
+ *                 SiLU gate of the Mamba block, "Temel Fikirler")
+ *
+ * The expanded (B,L,D,N) state never exists in device memory: it lives in
+ * registers, and only the contracted (B,L,D) output is written ("Donanım
+ * Duyarlı Durum Genişletme" section of the reading guide).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensors are dense, row-major, contiguous, in device memory.
+ *     (B,L,D) tensors: u, delta, z, y, dy, du, ddelta, dz.
+ *     (B,L,N) tensors: Bmat, Cmat, dB, dC.        (D,N): A, dA.
+ *     (D): Dskip, delta_bias, dD, ddelta_bias.    (B,D,N): h0, h_final, dh_final, dh0, state.
+ *   - io_dtype (SSM_F32 or SSM_BF16) is the storage type of u, delta, z,
+ *     Bmat, Cmat, y and of their gradients.  A, Dskip, delta_bias, every
+ *     state and dA, dD, ddelta_bias, dh0 are always fp32.  Arithmetic is fp32;
+ *     bf16 outputs are rounded to nearest even.
+ *   - Every pointer must be 16-byte aligned (ssm_state_update relaxes this,
+ *     see there); dim must be a multiple of 8;
+ *     dstate must be 1, 2, 4, 8 or 16; batch, seqlen, dim >= 1.
+ *   - The caller owns all memory.  The library never allocates, frees or
+ *     synchronises device memory; it enqueues kernels on hip_stream (a
+ *     hipStream_t; NULL = the default stream) and returns at once.
+ *   - Return value: SSM_OK or a positive ssm_status.  All arguments are
+ *     validated before anything is enqueued, so on error nothing is written.
+ *     ssm_last_error() gives a message for the last failing call on the
+ *     calling thread.  NaN and Inf in the inputs propagate; they are not
+ *     errors.
+ *   - Output buffers must not overlap input buffers (except state in
+ *     ssm_state_update, which is updated in place by design).
+ */
+#ifndef SSM_SCAN_H_
+#define SSM_SCAN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_SCAN_ABI_VERSION 1
+
+typedef enum ssm_status {
+  SSM_OK = 0,
+  SSM_ERR_NULL_ARG = 1,    /* a required pointer is NULL, or an optional pair is inconsistent */
+  SSM_ERR_BAD_SHAPE = 2,   /* a size is < 1 (or would overflow 64-bit offsets) */
+  SSM_ERR_UNSUPPORTED = 3, /* dstate not in {1,2,4,8,16}, dim % 8 != 0, unknown io_dtype */
+  SSM_ERR_ALIGNMENT = 4,   /* a pointer is not 16-byte aligned */
+  SSM_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns */
+  SSM_ERR_HIP = 6          /* the HIP runtime reported an error while enqueuing */
+} ssm_status;
+
+typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+/* SSM_SCAN_ABI_VERSION of the built library. */
+int ssm_abi_version(void);
+
+/* Static description of a status code ("ok", "null argument", ...). */
+const char *ssm_status_string(int status);
+
+/* Message of the last failing call on the calling thread ("" if none).  The
+ * pointer stays valid until the next library call on that thread. */
+const char *ssm_last_error(void);
+
+/* Number of time steps T between two saved chunk-boundary states. */
+int64_t ssm_scan_chunk_len(void);
+
+/* Bytes of the chunk_states buffer: batch * ceil(seqlen/T) * dim * dstate * 4.
+ * Layout (B, K, D, N) fp32, K = ceil(seqlen/T); slot k holds the state just
+ * before step k*T (slot 0 is h0, or zeros).  Returns -1 on invalid sizes. */
+int64_t ssm_scan_chunk_states_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+/* Device workspace the forward scan needs for these sizes (may be 0; then
+ * workspace may be NULL).  Returns -1 on invalid sizes. */
+int64_t ssm_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                     int io_dtype);
+
+/*
+ * Forward selective scan (the recurrence above over all L steps).
+ *
+ * Inputs:  u, delta (raw step size, before bias and softplus), z (optional
+ *          gate; NULL = no gate), Bmat, Cmat in io_dtype; A (D,N), Dskip
+ *          (optional, NULL = 0), delta_bias (optional, NULL = 0) fp32;
+ *          delta_softplus (0/1); h0 (optional initial state, NULL = zeros).
+ * Outputs: y (B,L,D) io_dtype; h_final (optional, NULL = not wanted) the
+ *          state after the last step; chunk_states (optional, NULL = not
+ *          wanted) the states at chunk boundaries, needed by ssm_scan_bwd.
+ * Workspace: ssm_scan_fwd_workspace_bytes() bytes of device memory, contents
+ *          undefined on entry and exit.
+ * Errors:  SSM_ERR_* as in the conventions; nothing is enqueued on error.
+ */
+int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                 const void *u, const void *delta, const float *A, const void *Bmat,
+                 const void *Cmat, const float *Dskip, const void *z, const float *delta_bias,
+                 int delta_softplus, const float *h0, float *h_final, void *y,
+                 float *chunk_states, void *workspace, int64_t workspace_bytes,
+                 void *hip_stream);
+
+/* Device workspace ssm_scan_bwd needs for these sizes.  -1 on invalid sizes. */
+int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                     int io_dtype);
+
+/*
+ * Backward of ssm_scan_fwd: gradients of a scalar loss given dy = dLoss/dy
+ * and (optionally) dh_final = dLoss/dh_final.  States inside a chunk are
+ * recomputed from chunk_states (written by ssm_scan_fwd with the same
+ * inputs) instead of being read from memory (reading guide, "Donanım Duyarlı
+ * Durum Genişletme": intermediate states are recomputed in the backward
+ * pass).
+ *
+ * Inputs:  the forward's inputs (same meaning, same pointers allowed),
+ *          chunk_states (required), dy (B,L,D) io_dtype, dh_final (optional).
+ * Outputs (all overwritten, never accumulated):
+ *          du, ddelta (w.r.t. the raw delta), dz (required iff z != NULL)
+ *          (B,L,D) io_dtype; dB, dC (B,L,N) io_dtype; dA (D,N) fp32;
+ *          dD (D) fp32, required iff Dskip != NULL; ddelta_bias (D) fp32,
+ *          optional; dh0 (B,D,N) fp32, optional.
+ * Workspace: ssm_scan_bwd_workspace_bytes() bytes, contents undefined.
+ * Sums over channels and time are fp32 in a fixed order: repeated calls give
+ * bit-identical results.
+ */
+int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                 const void *u, const void *delta, const float *A, const void *Bmat,
+                 const void *Cmat, const float *Dskip, const void *z, const float *delta_bias,
+                 int delta_softplus, const float *h0, const float *chunk_states, const void *dy,
+                 const float *dh_final, void *du, void *ddelta, float *dA, void *dB, void *dC,
+                 float *dD, void *dz, float *ddelta_bias, float *dh0, void *workspace,
+                 int64_t workspace_bytes, void *hip_stream);
+
+/*
+ * One decode step (reading guide, "Sorular", the question on KV caches: the
+ * model keeps a fixed D x N state per layer and advances it one token at a
+ * time).  state (B,D,N) fp32 is read once and overwritten in place with the
+ * new state; u, delta, z, y are (B,D) and Bmat, Cmat are (B,N) in io_dtype.
+ * Same arithmetic as one step of ssm_scan_fwd.  Alignment: state and A must be
+ * 16-byte aligned; the other pointers only need their element alignment.
+ */
+int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, float *state,
+                     const void *u, const void *delta, const float *A, const void *Bmat,
+                     const void *Cmat, const float *Dskip, const void *z,
+                     const float *delta_bias, int delta_softplus, void *y, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H_ */

@@ -1,0 +1,13 @@
+"""Selective-SSM scan for AMD MI355X (gfx950).
+
+Hand-written HIP kernels behind a C ABI (``include/ssm_scan.h``), with this
+package as a thin torch binding: the forward scan, its backward with
+recomputation from chunk-boundary states, and the single-token decode update
+of the Mamba selective state-space model (Gu & Dao, arXiv 2312.00752).
+"""
+from ._lib import EXPORTS, LIB_PATH, SSMError, load  # noqa: F401
+from .ops import (SelectiveScanFn, chunk_len, scan_bwd, scan_fwd, selective_scan,  # noqa: F401
+                  state_update)
+
+__all__ = ["scan_fwd", "scan_bwd", "state_update", "selective_scan", "SelectiveScanFn",
+           "chunk_len", "load", "SSMError"]

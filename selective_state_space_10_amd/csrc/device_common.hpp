@@ -1,0 +1,71 @@
+// device_common.hpp -- gfx950 device helpers shared by the scan kernels:
+// io-type loads/stores (fp32, bf16 with round-to-nearest-even), the step-size
+// nonlinearity (softplus) and the SiLU gate, built on the hardware exp2/log2/rcp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct bf16 {
+  uint16_t bits;
+};
+
+template <typename IO>
+struct io_traits;
+template <>
+struct io_traits<float> {
+  static constexpr int bytes = 4;
+};
+template <>
+struct io_traits<bf16> {
+  static constexpr int bytes = 2;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t x = __float_as_uint(f);
+  if ((x & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((x >> 16) | 0x40u);
+  x += 0x7fffu + ((x >> 16) & 1u);
+  return (uint16_t)(x >> 16);
+}
+
+__device__ __forceinline__ float load_io(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_io(const bf16* p, int64_t i) { return bf16_bits_to_f32(p[i].bits); }
+__device__ __forceinline__ void store_io(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void store_io(bf16* p, int64_t i, float v) { p[i].bits = f32_to_bf16_bits(v); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(s) = log(1 + e^s) = max(s, 0) + log1p(e^-|s|).
+// log1p(w) for w in (0, 1] is log(1 + w) corrected by the rounding error of
+// 1 + w: with v = fl(1 + w) and c = (v - 1) - w (exact), log1p(w) = log(v) - c
+// up to a relative 2^-24 term.  No branch; for large |s| the log term is e^-|s|.
+__device__ __forceinline__ float softplus_f(float s) {
+  const float w = fast_exp2(-fabsf(s) * kLog2e);
+  const float v = 1.0f + w;
+  const float c = (v - 1.0f) - w;
+  const float l = fast_log2(v) * kLn2 - c;
+  return fmaxf(s, 0.0f) + l;
+}
+
+// logistic sigmoid 1 / (1 + e^-x); saturates to 0 / 1 without NaN for finite x.
+__device__ __forceinline__ float sigmoid_f(float x) { return fast_rcp(1.0f + fast_exp2(-x * kLog2e)); }
+
+__device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
+
+// Step size from the raw input: softplus(raw + bias) or raw + bias.
+__device__ __forceinline__ float step_size(float raw, float bias, bool softplus) {
+  const float s = raw + bias;
+  return softplus ? softplus_f(s) : s;
+}
+
+}  // namespace ssm

@@ -1,0 +1,55 @@
+// kernels.hpp -- argument blocks and launchers shared by the C-ABI layer
+// (ssm_api.cpp) and the HIP kernel files.  Sizes here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// Steps between two saved chunk-boundary states (the forward writes the state
+// before every multiple of this step; the backward recomputes within chunks).
+constexpr int64_t kChunkLen = 256;
+
+struct FwdArgs {
+  int64_t B, L, D, N;
+  const void *u, *delta, *Bm, *Cm, *z;
+  const float *A, *Dskip, *bias, *h0;
+  int softplus;
+  float *h_final;
+  void *y;
+  float *chunk_states;
+  void *workspace;
+  int64_t workspace_bytes;
+};
+
+struct BwdArgs {
+  int64_t B, L, D, N;
+  const void *u, *delta, *Bm, *Cm, *z, *dy;
+  const float *A, *Dskip, *bias, *h0, *chunk_states, *dh_final;
+  int softplus;
+  void *du, *ddelta, *dB, *dC, *dz;
+  float *dA, *dD, *dbias, *dh0;
+  void *workspace;
+  int64_t workspace_bytes;
+};
+
+struct DecodeArgs {
+  int64_t B, D, N;
+  float *state;
+  const void *u, *delta, *Bm, *Cm, *z;
+  const float *A, *Dskip, *bias;
+  int softplus;
+  void *y;
+};
+
+int64_t fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype);
+int64_t bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype);
+
+// Each launcher enqueues its kernels on `stream` and returns the first HIP
+// error reported while enqueuing (hipSuccess otherwise).
+hipError_t launch_fwd(const FwdArgs &a, int io_dtype, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs &a, int io_dtype, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, int io_dtype, hipStream_t stream);
+
+}  // namespace ssm

@@ -1,0 +1,91 @@
+// state_update.hip -- one decode step of the selective SSM (reading guide of
+// arXiv 2312.00752, "Sorular", question on KV caches: a fixed D x N state per
+// layer advanced one token at a time).  The (B,D,N) fp32 state is streamed
+// once in and once out with 16-byte accesses; everything else is small.
+//
+// Mapping: each lane owns SPL = min(N, 4) consecutive states of one channel,
+// LPC = N / SPL lanes share a channel (adjacent lanes), so a wave reads and
+// writes one contiguous 1 KiB span of the state.  The per-channel prologue is
+// recomputed by the LPC lanes of the channel (cheaper than sharing it), the
+// partial sum_n C h is reduced across them with cross-lane adds, and the first
+// lane of the group stores y.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace ssm {
+
+template <typename IO, int N>
+__global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
+  constexpr int SPL = N < 4 ? N : 4;
+  constexpr int LPC = N / SPL;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t ch = gid / LPC;  // b * D + d
+  const int g = (int)(gid % LPC);
+  const bool valid = ch < a.B * a.D;
+  const int64_t chc = valid ? ch : 0;
+  const int64_t b = chc / a.D, d = chc % a.D;
+  const IO *u = (const IO *)a.u, *dl = (const IO *)a.delta, *zz = (const IO *)a.z;
+  const IO *Bm = (const IO *)a.Bm, *Cm = (const IO *)a.Cm;
+
+  float st[SPL], Av[SPL];
+  float *sp = a.state + chc * N + g * SPL;
+  if constexpr (SPL == 4) {
+    const float4 v = *(const float4 *)sp;
+    st[0] = v.x, st[1] = v.y, st[2] = v.z, st[3] = v.w;
+    const float4 q = *(const float4 *)(a.A + d * N + g * SPL);
+    Av[0] = q.x, Av[1] = q.y, Av[2] = q.z, Av[3] = q.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) st[k] = sp[k], Av[k] = a.A[d * N + g * SPL + k];
+  }
+  const float x = load_io(u, chc);
+  const float dt = step_size(load_io(dl, chc), a.bias ? a.bias[d] : 0.0f, a.softplus != 0);
+  const float dtu = dt * x;
+  float ys = 0.0f;
+#pragma unroll
+  for (int k = 0; k < SPL; ++k) {
+    const int64_t bn = b * N + g * SPL + k;
+    st[k] = fmaf(fast_exp2(dt * Av[k] * kLog2e), st[k], dtu * load_io(Bm, bn));
+    ys = fmaf(load_io(Cm, bn), st[k], ys);
+  }
+#pragma unroll
+  for (int off = 1; off < LPC; off <<= 1) ys += __shfl_xor(ys, off, 64);
+  if (!valid) return;
+  if constexpr (SPL == 4) {
+    *(float4 *)sp = make_float4(st[0], st[1], st[2], st[3]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) sp[k] = st[k];
+  }
+  if (g == 0) {
+    float out = fmaf(a.Dskip ? a.Dskip[d] : 0.0f, x, ys);
+    if (a.z) out *= silu_f(load_io(zz, chc));
+    store_io((IO *)a.y, chc, out);
+  }
+}
+
+template <typename IO, int N>
+static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
+  constexpr int LPC = N < 4 ? 1 : N / 4;
+  const int64_t threads = a.B * a.D * LPC;
+  hipLaunchKernelGGL((decode_kernel<IO, N>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename IO>
+static hipError_t launch_decode_io(const DecodeArgs &a, hipStream_t s) {
+  switch (a.N) {
+    case 1: return launch_decode_t<IO, 1>(a, s);
+    case 2: return launch_decode_t<IO, 2>(a, s);
+    case 4: return launch_decode_t<IO, 4>(a, s);
+    case 8: return launch_decode_t<IO, 8>(a, s);
+    case 16: return launch_decode_t<IO, 16>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeArgs &a, int io_dtype, hipStream_t s) {
+  return io_dtype == 0 ? launch_decode_io<float>(a, s) : launch_decode_io<bf16>(a, s);
+}
+
+}  // namespace ssm

@@ -1,0 +1,187 @@
+"""Torch-facing wrappers of the C ABI: shape/dtype/device checks, output and
+workspace allocation with ``torch.empty``, and the call on the current stream.
+Every step of the scan itself runs in the HIP library; nothing here computes.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_IO = {torch.float32: _lib.SSM_F32, torch.bfloat16: _lib.SSM_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(name, t, shape, dtype, device, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _io_code(u: torch.Tensor) -> int:
+    if u.dtype not in _IO:
+        raise TypeError(f"io dtype must be float32 or bfloat16, got {u.dtype}")
+    return _IO[u.dtype]
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def chunk_len() -> int:
+    return int(_lib.load().ssm_scan_chunk_len())
+
+
+def _check_common(u, delta, A, B, C, D, z, delta_bias, h0):
+    if not isinstance(u, torch.Tensor) or u.dim() != 3:
+        raise ValueError("u must be a (batch, seqlen, dim) tensor")
+    if not isinstance(A, torch.Tensor) or A.dim() != 2:
+        raise ValueError("A must be a (dim, dstate) tensor")
+    Bsz, L, Dm = u.shape
+    N = A.shape[1]
+    dev, io = u.device, u.dtype
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {dev}")
+    _io_code(u)
+    _need("u", u, (Bsz, L, Dm), io, dev)
+    _need("delta", delta, (Bsz, L, Dm), io, dev)
+    _need("A", A, (Dm, N), torch.float32, dev)
+    _need("B", B, (Bsz, L, N), io, dev)
+    _need("C", C, (Bsz, L, N), io, dev)
+    _need("D", D, (Dm,), torch.float32, dev, optional=True)
+    _need("z", z, (Bsz, L, Dm), io, dev, optional=True)
+    _need("delta_bias", delta_bias, (Dm,), torch.float32, dev, optional=True)
+    _need("h0", h0, (Bsz, Dm, N), torch.float32, dev, optional=True)
+    return Bsz, L, Dm, N
+
+
+def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, h0=None,
+             return_final_state=False, save_chunk_states=False):
+    """Forward selective scan.  Returns (y, h_final or None, chunk_states or None)."""
+    Bsz, L, Dm, N = _check_common(u, delta, A, B, C, D, z, delta_bias, h0)
+    lib = _lib.load()
+    io = _io_code(u)
+    dev = u.device
+    y = torch.empty_like(u)
+    hf = torch.empty((Bsz, Dm, N), dtype=torch.float32, device=dev) if return_final_state else None
+    cs = None
+    if save_chunk_states:
+        K = -(-L // chunk_len())
+        cs = torch.empty((Bsz, K, Dm, N), dtype=torch.float32, device=dev)
+    wsb = int(lib.ssm_scan_fwd_workspace_bytes(Bsz, L, Dm, N, io))
+    if wsb < 0:
+        raise ValueError("invalid sizes for the forward workspace query")
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb > 0 else None
+    with torch.cuda.device(dev):
+        st = lib.ssm_scan_fwd(Bsz, L, Dm, N, io, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                              _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)),
+                              _ptr(h0), _ptr(hf), _ptr(y), _ptr(cs), _ptr(ws), wsb, _stream(dev))
+    _lib.check(st)
+    return y, hf, cs
+
+
+def scan_bwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, chunk_states, dy,
+             dh_final=None, want_ddelta_bias=True, want_dh0=True):
+    """Backward of scan_fwd.  Returns a dict: du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0."""
+    Bsz, L, Dm, N = _check_common(u, delta, A, B, C, D, z, delta_bias, h0)
+    lib = _lib.load()
+    io = _io_code(u)
+    dev = u.device
+    K = -(-L // chunk_len())
+    _need("chunk_states", chunk_states, (Bsz, K, Dm, N), torch.float32, dev)
+    _need("dy", dy, (Bsz, L, Dm), u.dtype, dev)
+    _need("dh_final", dh_final, (Bsz, Dm, N), torch.float32, dev, optional=True)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(u), dA=torch.empty((Dm, N), **f32),
+             dB=torch.empty_like(B), dC=torch.empty_like(C),
+             dD=torch.empty((Dm,), **f32) if D is not None else None,
+             dz=torch.empty_like(u) if z is not None else None,
+             ddelta_bias=torch.empty((Dm,), **f32) if (delta_bias is not None and want_ddelta_bias)
+             else None,
+             dh0=torch.empty((Bsz, Dm, N), **f32) if want_dh0 else None)
+    wsb = int(lib.ssm_scan_bwd_workspace_bytes(Bsz, L, Dm, N, io))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = lib.ssm_scan_bwd(Bsz, L, Dm, N, io, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                              _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)),
+                              _ptr(h0), _ptr(chunk_states), _ptr(dy), _ptr(dh_final),
+                              _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                              _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]),
+                              _ptr(g["dh0"]), _ptr(ws), wsb, _stream(dev))
+    _lib.check(st)
+    return g
+
+
+def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True):
+    """One decode step; ``state`` (batch, dim, dstate) fp32 is updated in place.  Returns y."""
+    if not isinstance(state, torch.Tensor) or state.dim() != 3:
+        raise ValueError("state must be a (batch, dim, dstate) tensor")
+    Bsz, Dm, N = state.shape
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {dev}")
+    if not isinstance(u, torch.Tensor):
+        raise TypeError("u must be a torch.Tensor")
+    io = _io_code(u)
+    _need("state", state, (Bsz, Dm, N), torch.float32, dev)
+    _need("u", u, (Bsz, Dm), u.dtype, dev)
+    _need("delta", delta, (Bsz, Dm), u.dtype, dev)
+    _need("A", A, (Dm, N), torch.float32, dev)
+    _need("B", B, (Bsz, N), u.dtype, dev)
+    _need("C", C, (Bsz, N), u.dtype, dev)
+    _need("D", D, (Dm,), torch.float32, dev, optional=True)
+    _need("z", z, (Bsz, Dm), u.dtype, dev, optional=True)
+    _need("delta_bias", delta_bias, (Dm,), torch.float32, dev, optional=True)
+    lib = _lib.load()
+    y = torch.empty_like(u)
+    with torch.cuda.device(dev):
+        st = lib.ssm_state_update(Bsz, Dm, N, io, _ptr(state), _ptr(u), _ptr(delta), _ptr(A),
+                                  _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                  int(bool(delta_softplus)), _ptr(y), _stream(dev))
+    _lib.check(st)
+    return y
+
+
+class SelectiveScanFn(torch.autograd.Function):
+    """Autograd wrapper: forward saves the chunk-boundary states, backward
+    recomputes the states inside each chunk from them."""
+
+    @staticmethod
+    def forward(ctx, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                h0=None):
+        y, hf, cs = scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0,
+                             return_final_state=True, save_chunk_states=True)
+        ctx.delta_softplus = bool(delta_softplus)
+        ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, h0, cs)
+        return y, hf
+
+    @staticmethod
+    def backward(ctx, dy, dhf):
+        u, delta, A, B, C, D, z, delta_bias, h0, cs = ctx.saved_tensors
+        g = scan_bwd(u, delta, A, B, C, D, z, delta_bias, ctx.delta_softplus, h0, cs,
+                     dy.contiguous(), None if dhf is None else dhf.contiguous(),
+                     want_ddelta_bias=delta_bias is not None, want_dh0=h0 is not None)
+        return (g["du"], g["ddelta"], g["dA"], g["dB"], g["dC"], g["dD"], g["dz"],
+                g["ddelta_bias"], None, g["dh0"])
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                   h0=None):
+    """Differentiable scan; returns (y, h_final)."""
+    return SelectiveScanFn.apply(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0)

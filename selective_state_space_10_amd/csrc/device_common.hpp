@@ -41,6 +41,33 @@ __device__ __forceinline__ float load_io(const bf16* p, int64_t i) { return bf16
 __device__ __forceinline__ void store_io(float* p, int64_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void store_io(bf16* p, int64_t i, float v) { p[i].bits = f32_to_bf16_bits(v); }
 
+// Four consecutive elements (16 B of fp32, 8 B of bf16); the index is a
+// multiple of 4 and the base is 16-byte aligned.
+template <typename IO>
+struct Vec4;
+template <>
+struct Vec4<float> {
+  typedef float4 raw;
+  static __device__ __forceinline__ raw load(const float *p, int64_t i) { return *(const float4 *)(p + i); }
+  static __device__ __forceinline__ float4 cvt(raw r) { return r; }
+  static __device__ __forceinline__ void store(float *p, int64_t i, float4 v) { *(float4 *)(p + i) = v; }
+};
+template <>
+struct Vec4<bf16> {
+  typedef uint2 raw;
+  static __device__ __forceinline__ raw load(const bf16 *p, int64_t i) { return *(const uint2 *)(p + i); }
+  static __device__ __forceinline__ float4 cvt(raw r) {
+    return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+  }
+  static __device__ __forceinline__ void store(bf16 *p, int64_t i, float4 v) {
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16);
+    o.y = (uint32_t)f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16);
+    *(uint2 *)(p + i) = o;
+  }
+};
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }

@@ -8,196 +8,289 @@
 // "Donanım Duyarlı Durum Genişletme" section: the expanded state is never
 // materialised in device memory).
 //
-// Mapping (one workgroup = 64 consecutive channels of one batch row):
-//   - lanes <-> channels d, so every (B,L,D) access of a wave is 64
-//     consecutive elements (coalesced);
-//   - the N states of a channel are split over NW = N/NPL waves, NPL states
-//     per lane, so that the 16-state problems put 2 waves on every SIMD;
-//   - time is processed in chunks of T steps.  For each chunk, every thread
-//     computes the per-(t,d) prologue (dt, dt*u) for T/NW of the steps once
-//     and shares it through LDS; each wave then runs the recurrence for its
-//     states over the T steps, reading B and C as wave-uniform scalar loads,
-//     and leaves its partial sum_n C h in LDS; finally every thread reduces
-//     the partials over waves for its steps, adds D*u, applies the gate and
-//     stores y.  Global loads of the next chunk are issued before the
-//     recurrence of the current one so they are in flight while it runs.
-#include <type_traits>
+// One workgroup owns 64 consecutive channels of one batch row and walks the
+// sequence in chunks of T steps:
+//   - Cooperative phases (all threads): every thread owns fixed (step, group of
+//     4 channels) items of a chunk and moves them with 16-byte (fp32) or
+//     8-byte (bf16) accesses.  The prologue turns (delta, u) into (dt, dt*u)
+//     and stores them in LDS once per (t, d); it also stages the chunk's B and
+//     C rows in LDS.  The epilogue adds the per-wave partial sums, applies
+//     D*u and the SiLU gate, and stores y.
+//   - Recurrence (one wave per NPL states): lanes are channels, so the 2-state
+//     slices of the 16-state problem put 8 waves (2 per SIMD) on the 64
+//     channels.  Each step reads (dt, dt*u) for its lane and the wave's
+//     B/C values from LDS, updates the states, and leaves sum_n C h in LDS.
+//   - Loads run PD chunks ahead in registers, so that several chunks of
+//     input are in flight while the recurrence of the current one executes.
+#include <stdlib.h>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace ssm {
 
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(4))) const float cfloat4_t;
-typedef __attribute__((address_space(4))) const f32x2_t cfloat2_4_t;
-typedef __attribute__((address_space(4))) const uint32_t cuint4_t;
+template <typename IO, int N, int NPL, int CPW, int T, int PD>
+__global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs a) {
+  constexpr int NG = 64 / CPW;             // state groups per wave (lanes = CPW channels x NG groups)
+  constexpr int NW = N / (NPL * NG);       // waves per workgroup
+  constexpr int NT = 64 * NW;              // threads
+  constexpr int NSP = N / NPL;             // state slices per channel
+  constexpr int G = CPW / 4;               // groups of 4 channels per tile
+  constexpr int IPT = T * G / NT;          // (step, channel group) items per thread per chunk
+  constexpr int BCN = T * N;               // B (and C) values per chunk
+  constexpr int BPT = (BCN + NT - 1) / NT;
+  static_assert(NW >= 1 && NSP == NW * NG, "states must split evenly over lanes and waves");
+  static_assert((T * G) % NT == 0 && IPT >= 1, "items must split evenly over threads");
+  static_assert(NT % G == 0, "a thread's channel group must not change between items");
+  using V = Vec4<IO>;
+  typedef typename V::raw raw_t;
 
-// Wave-uniform loads of NPL consecutive values (B or C for a wave's states)
-// through the scalar unit.  `i` is a multiple of NPL.
-template <int NPL>
-__device__ __forceinline__ void uniform_load(const float *p, int64_t i, float *out) {
-  if constexpr (NPL == 2) {
-    const f32x2_t v = ((cfloat2_4_t *)(p + i))[0];
-    out[0] = v.x;
-    out[1] = v.y;
-  } else {
-#pragma unroll
-    for (int k = 0; k < NPL; ++k) out[k] = ((cfloat4_t *)p)[i + k];
-  }
-}
-// bf16: for NPL = 2 the pair is one aligned dword (p + i is 4-byte aligned
-// because N is even); a single bf16 value is read with an ordinary load.
-template <int NPL>
-__device__ __forceinline__ void uniform_load(const bf16 *p, int64_t i, float *out) {
-  if constexpr (NPL == 2) {
-    const uint32_t bits = ((cuint4_t *)(p + i))[0];
-    out[0] = __uint_as_float(bits << 16);
-    out[1] = __uint_as_float(bits & 0xffff0000u);
-  } else {
-#pragma unroll
-    for (int k = 0; k < NPL; ++k) out[k] = load_io(p, i + k);
-  }
-}
-
-template <typename IO, int N, int NPL, int T>
-__global__ void __launch_bounds__(64 * (N / NPL)) fwd_chunked_kernel(FwdArgs a) {
-  constexpr int NW = N / NPL;
-  constexpr int TPW = T / NW;  // prologue/epilogue steps per thread per chunk
-  static_assert(T % NW == 0, "chunk must split evenly over waves");
   const IO *__restrict__ u = (const IO *)a.u;
   const IO *__restrict__ dl = (const IO *)a.delta;
   const IO *__restrict__ zz = (const IO *)a.z;
-  const IO *Bm = (const IO *)a.Bm;
-  const IO *Cm = (const IO *)a.Cm;
+  const IO *__restrict__ Bm = (const IO *)a.Bm;
+  const IO *__restrict__ Cm = (const IO *)a.Cm;
   IO *__restrict__ y = (IO *)a.y;
 
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t L = a.L, D = a.D;
   const int64_t b = blockIdx.y;
-  const int64_t d = (int64_t)blockIdx.x * 64 + lane;
-  const bool dv = d < D;
-  const int64_t dc = dv ? d : D - 1;  // clamped channel for loads
-  const bool has_z = a.z != nullptr;
-  const bool sp = a.softplus != 0;
-
-  __shared__ float2 P[T][64];        // (dt, dt*u) per step and channel
-  __shared__ float Y[T][NW][64];     // per-wave partial sum_n C h
-
-  float Ap[NPL], h[NPL];
-#pragma unroll
-  for (int k = 0; k < NPL; ++k) {
-    const int n = w * NPL + k;
-    Ap[k] = a.A[dc * N + n] * kLog2e;
-    h[k] = a.h0 ? a.h0[(b * D + dc) * N + n] : 0.0f;
-  }
-  const float bias = a.bias ? a.bias[dc] : 0.0f;
-  const float Dv = a.Dskip ? a.Dskip[dc] : 0.0f;
-
-  float r_raw[TPW], r_u[TPW], r_z[TPW];   // loads in flight for the next chunk
-  float keep_u[TPW], keep_g[TPW];         // kept for the epilogue
+  const int64_t d0 = (int64_t)blockIdx.x * CPW;
   const int64_t row0 = b * L;
   const int64_t nck = (L + T - 1) / T;
   const int64_t K = (L + kChunkLen - 1) / kChunkLen;
+  const bool has_z = a.z != nullptr;
+  const bool sp = a.softplus != 0;
 
-  auto load_chunk = [&](int64_t k) {
+  __shared__ __attribute__((aligned(16))) float2 P[T][CPW];         // (dt, dt*u) per step and channel
+  __shared__ __attribute__((aligned(16))) float Y[T][NW][64];       // per-lane partial sum over its states
+  __shared__ __attribute__((aligned(16))) float BC[T][NSP][2 * NPL];  // B then C values per state slice
+
+  // --- cooperative-phase ownership: channel group g, steps tl0 + j*(NT/G)
+  const int g = tid % G;
+  const int tl0 = tid / G;
+  const int64_t dg = d0 + 4 * g;
+  const bool gv = dg < D;                      // D % 4 == 0: a group is all valid or all not
+  const int64_t dgc = gv ? dg : D - 4;
+  float bias4[4] = {0.f, 0.f, 0.f, 0.f}, Dsk4[4] = {0.f, 0.f, 0.f, 0.f};
+  if (a.bias) {
+    const float4 v = *(const float4 *)(a.bias + dgc);
+    bias4[0] = v.x, bias4[1] = v.y, bias4[2] = v.z, bias4[3] = v.w;
+  }
+  if (a.Dskip) {
+    const float4 v = *(const float4 *)(a.Dskip + dgc);
+    Dsk4[0] = v.x, Dsk4[1] = v.y, Dsk4[2] = v.z, Dsk4[3] = v.w;
+  }
+
+  // --- recurrence ownership: channel d0 + c, state slice spi = w*NG + gi
+  const int c = lane % CPW;
+  const int gi = lane / CPW;
+  const int spi = w * NG + gi;
+  const int64_t d = d0 + c;
+  const bool dv = d < D;
+  const int64_t dc = dv ? d : D - 1;
+  float Ap[NPL], h[NPL];
 #pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-      const int64_t t = k * T + w * TPW + j;
-      const int64_t idx = (row0 + (t < L ? t : L - 1)) * D + dc;
-      r_raw[j] = load_io(dl, idx);
-      r_u[j] = load_io(u, idx);
-      r_z[j] = has_z ? load_io(zz, idx) : 0.0f;
+  for (int k = 0; k < NPL; ++k) {
+    const int n = spi * NPL + k;
+    Ap[k] = a.A[dc * N + n] * kLog2e;
+    h[k] = a.h0 ? a.h0[(b * D + dc) * N + n] : 0.0f;
+  }
+
+  raw_t r_raw[PD][IPT], r_u[PD][IPT], r_z[PD][IPT];  // loads in flight
+  float r_b[PD][BPT], r_c[PD][BPT];
+  float4 keep_u[IPT], keep_g[IPT];                     // kept for the epilogue
+
+  auto load_chunk = [&](int64_t k, raw_t(&ra)[IPT], raw_t(&ru)[IPT], raw_t(&rz)[IPT], float(&rb)[BPT],
+                        float(&rc)[BPT]) {
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int64_t t = k * T + tl0 + j * (NT / G);
+      const int64_t idx = (row0 + (t < L ? t : L - 1)) * D + dgc;
+      ra[j] = V::load(dl, idx);
+      ru[j] = V::load(u, idx);
+      if (has_z) rz[j] = V::load(zz, idx);
     }
-  };
-  auto prologue = [&](int64_t k) {
 #pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-      const int tl = w * TPW + j;
-      const int64_t t = k * T + tl;
-      float dt = 0.0f, dtu = 0.0f;  // steps past the end leave the state unchanged
-      if (t < L) {
-        dt = step_size(r_raw[j], bias, sp);
-        dtu = dt * r_u[j];
+    for (int j = 0; j < BPT; ++j) {
+      const int i = tid + j * NT;
+      if (BCN % NT == 0 || i < BCN) {
+        const int64_t t = k * T + i / N;
+        const int64_t idx = (row0 + (t < L ? t : L - 1)) * N + i % N;
+        rb[j] = load_io(Bm, idx);
+        rc[j] = load_io(Cm, idx);
       }
-      P[tl][lane] = make_float2(dt, dtu);
-      keep_u[j] = r_u[j];
-      keep_g[j] = has_z ? silu_f(r_z[j]) : 1.0f;
     }
   };
-
-  load_chunk(0);
-  prologue(0);
-  __syncthreads();
-  for (int64_t k = 0; k < nck; ++k) {
+  auto prologue = [&](int64_t k, raw_t(&ra)[IPT], raw_t(&ru)[IPT], raw_t(&rz)[IPT], float(&rb)[BPT],
+                      float(&rc)[BPT]) {
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int tl = tl0 + j * (NT / G);
+      const bool tv = k * T + tl < L;  // steps past the end get dt = 0: no state change
+      const float4 r = V::cvt(ra[j]), x = V::cvt(ru[j]);
+      const float rv[4] = {r.x, r.y, r.z, r.w}, xv[4] = {x.x, x.y, x.z, x.w};
+      float dt[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dt[q] = tv ? step_size(rv[q], bias4[q], sp) : 0.0f;
+      float4 *pp = (float4 *)&P[tl][4 * g];
+      pp[0] = make_float4(dt[0], dt[0] * xv[0], dt[1], dt[1] * xv[1]);
+      pp[1] = make_float4(dt[2], dt[2] * xv[2], dt[3], dt[3] * xv[3]);
+      keep_u[j] = x;
+      if (has_z) {
+        const float4 zv = V::cvt(rz[j]);
+        keep_g[j] = make_float4(silu_f(zv.x), silu_f(zv.y), silu_f(zv.z), silu_f(zv.w));
+      } else {
+        keep_g[j] = make_float4(1.f, 1.f, 1.f, 1.f);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int i = tid + j * NT;
+      if (BCN % NT == 0 || i < BCN) {
+        const int tl = i / N, n = i % N;
+        BC[tl][n / NPL][n % NPL] = rb[j];
+        BC[tl][n / NPL][NPL + n % NPL] = rc[j];
+      }
+    }
+  };
+  auto epilogue = [&](int64_t k) {
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int tl = tl0 + j * (NT / G);
+      const int64_t t = k * T + tl;
+      if (t < L && gv) {
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+#pragma unroll
+          for (int gg = 0; gg < NG; ++gg) {
+            const float4 v = *(const float4 *)&Y[tl][ww][gg * CPW + 4 * g];
+            s.x += v.x, s.y += v.y, s.z += v.z, s.w += v.w;
+          }
+        }
+        s.x = fmaf(Dsk4[0], keep_u[j].x, s.x) * keep_g[j].x;
+        s.y = fmaf(Dsk4[1], keep_u[j].y, s.y) * keep_g[j].y;
+        s.z = fmaf(Dsk4[2], keep_u[j].z, s.z) * keep_g[j].z;
+        s.w = fmaf(Dsk4[3], keep_u[j].w, s.w) * keep_g[j].w;
+        V::store(y, (row0 + t) * D + dg, s);
+      }
+    }
+  };
+  auto scan_chunk = [&](int64_t k) {
     const int64_t t0 = k * T;
     if (a.chunk_states && (t0 % kChunkLen) == 0 && dv) {
-      float *cs = a.chunk_states + ((b * K + t0 / kChunkLen) * D + d) * N + w * NPL;
+      float *cs = a.chunk_states + ((b * K + t0 / kChunkLen) * D + d) * N + spi * NPL;
 #pragma unroll
       for (int kk = 0; kk < NPL; ++kk) cs[kk] = h[kk];
     }
-    if (k + 1 < nck) load_chunk(k + 1);
-    // B and C rows of this chunk for this wave's states; in a full chunk the
-    // per-step offsets are constants, in the ragged last chunk they are
-    // clamped to the last row (those steps have dt = 0 and change nothing).
-    const IO *Bp = Bm + (row0 + t0) * N + w * NPL;
-    const IO *Cp = Cm + (row0 + t0) * N + w * NPL;
-    auto scan_steps = [&](auto full) {
 #pragma unroll
-      for (int tl = 0; tl < T; ++tl) {
-        int64_t off = (int64_t)tl * N;
-        if constexpr (!decltype(full)::value) {
-          if (t0 + tl >= L) off = (L - 1 - t0) * N;
-        }
-        const float2 p = P[tl][lane];
-        float Bv[NPL], Cv[NPL];
-        uniform_load<NPL>(Bp, off, Bv);
-        uniform_load<NPL>(Cp, off, Cv);
-        float ys = 0.0f;
+    for (int tl = 0; tl < T; ++tl) {
+      const float2 p = P[tl][c];
+      float bc[2 * NPL];
+      if constexpr (NPL == 2) {
+        const float4 q = *(const float4 *)&BC[tl][spi][0];
+        bc[0] = q.x, bc[1] = q.y, bc[2] = q.z, bc[3] = q.w;
+      } else {
 #pragma unroll
-        for (int kk = 0; kk < NPL; ++kk) {
-          const float da = fast_exp2(p.x * Ap[kk]);
-          h[kk] = fmaf(da, h[kk], p.y * Bv[kk]);
-          ys = fmaf(Cv[kk], h[kk], ys);
-        }
-        Y[tl][w][lane] = ys;
+        for (int q = 0; q < 2 * NPL; ++q) bc[q] = BC[tl][spi][q];
       }
-    };
-    if (t0 + T <= L)
-      scan_steps(std::true_type{});
-    else
-      scan_steps(std::false_type{});
-    __syncthreads();
+      float ys = 0.0f;
 #pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-      const int tl = w * TPW + j;
-      const int64_t t = t0 + tl;
-      if (t < L && dv) {
-        float s = 0.0f;
+      for (int kk = 0; kk < NPL; ++kk) {
+        const float da = fast_exp2(p.x * Ap[kk]);
+        h[kk] = fmaf(da, h[kk], p.y * bc[kk]);
+        ys = fmaf(bc[NPL + kk], h[kk], ys);
+      }
+      Y[tl][w][lane] = ys;
+    }
+  };
+
+  // Prime the pipeline: chunks 0 .. PD-1 in flight, prologue of chunk 0.
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) s += Y[tl][ww][lane];
-        s = fmaf(Dv, keep_u[j], s) * keep_g[j];
-        store_io(y, (row0 + t) * D + d, s);
+  for (int s = 0; s < PD; ++s)
+    if (s < nck) load_chunk(s, r_raw[s], r_u[s], r_z[s], r_b[s], r_c[s]);
+  prologue(0, r_raw[0], r_u[0], r_z[0], r_b[0], r_c[0]);
+  __syncthreads();
+  // Chunk k uses ring slot k % PD; the loop is unrolled by PD so slots are
+  // compile-time register arrays.
+  for (int64_t k0 = 0; k0 < nck; k0 += PD) {
+#pragma unroll
+    for (int s = 0; s < PD; ++s) {
+      const int64_t k = k0 + s;
+      if (k < nck) {
+        if (k + PD < nck) load_chunk(k + PD, r_raw[s], r_u[s], r_z[s], r_b[s], r_c[s]);
+        scan_chunk(k);
+        __syncthreads();
+        epilogue(k);
+        const int sn = (s + 1) % PD;
+        if (k + 1 < nck) prologue(k + 1, r_raw[sn], r_u[sn], r_z[sn], r_b[sn], r_c[sn]);
+        __syncthreads();
       }
     }
-    if (k + 1 < nck) prologue(k + 1);
-    __syncthreads();
   }
   if (a.h_final && dv) {
 #pragma unroll
-    for (int kk = 0; kk < NPL; ++kk) a.h_final[(b * D + d) * N + w * NPL + kk] = h[kk];
+    for (int kk = 0; kk < NPL; ++kk) a.h_final[(b * D + d) * N + spi * NPL + kk] = h[kk];
   }
+}
+
+// Channels per workgroup (CPW) for dstate N.  A 64-channel tile needs 84 KB
+// of LDS (one workgroup per CU); 32- and 16-channel tiles fit 3 and 6 per CU.
+// Measured on MI355X: 64-channel tiles are fastest while the grid fits in one
+// round over the CUs; beyond that, 32-channel tiles avoid a mostly idle
+// second round.  SSM_FWD_CPW overrides the choice (tuning only).
+static int device_cus() {
+  static int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return 256;
+    return n;
+  }();
+  return cus;
+}
+
+template <int N>
+static int pick_cpw(const FwdArgs &a) {
+  static const int env = [] {
+    const char *e = getenv("SSM_FWD_CPW");
+    return e ? atoi(e) : 0;
+  }();
+  constexpr int NPL = N >= 2 ? 2 : 1;
+  constexpr int mincpw = 64 * NPL / N > 16 ? 64 * NPL / N : 16;
+  if (env == 16 || env == 32 || env == 64) return env < mincpw ? mincpw : env;
+  const int64_t wg64 = a.B * ((a.D + 63) / 64);
+  if (wg64 <= device_cus() || mincpw > 32) return 64;
+  return 32;
+}
+
+template <typename IO, int N, int CPW>
+static hipError_t launch_fwd_cpw(const FwdArgs &a, hipStream_t s) {
+  constexpr int NPL = N >= 2 ? 2 : 1;
+  constexpr int NW = N * CPW / (64 * NPL);
+  constexpr int T = 32;
+  constexpr int IPT = T * (CPW / 4) / (64 * NW);
+  constexpr int PD = IPT <= 2 ? 2 : 1;
+  dim3 grid((unsigned)((a.D + CPW - 1) / CPW), (unsigned)a.B);
+  hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD>), grid, dim3(64 * NW), 0, s, a);
+  return hipGetLastError();
 }
 
 template <typename IO, int N>
 static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
   constexpr int NPL = N >= 2 ? 2 : 1;
-  constexpr int NW = N / NPL;
-  constexpr int T = 16;
-  dim3 grid((unsigned)((a.D + 63) / 64), (unsigned)a.B);
-  hipLaunchKernelGGL((fwd_chunked_kernel<IO, N, NPL, T>), grid, dim3(64 * NW), 0, s, a);
-  return hipGetLastError();
+  constexpr int mincpw = 64 * NPL / N > 16 ? 64 * NPL / N : 16;
+  const int cpw = pick_cpw<N>(a);
+  if constexpr (mincpw <= 16) {
+    if (cpw == 16) return launch_fwd_cpw<IO, N, 16>(a, s);
+  }
+  if constexpr (mincpw <= 32) {
+    if (cpw == 32) return launch_fwd_cpw<IO, N, 32>(a, s);
+  }
+  return launch_fwd_cpw<IO, N, 64>(a, s);
 }
 
 template <typename IO>

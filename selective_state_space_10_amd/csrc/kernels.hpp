@@ -21,6 +21,11 @@ struct FwdArgs {
   float *chunk_states;
   void *workspace;
   int64_t workspace_bytes;
+  // sequence split (set by the launcher): segment length in steps (0 = one
+  // segment), per-segment local end states, summed step sizes, and the true
+  // states entering each segment; all (B, nseg, D[, N]) fp32 in the workspace
+  int64_t seg_len;
+  float *seg_hloc, *seg_dsum, *seg_state;
 };
 
 struct BwdArgs {

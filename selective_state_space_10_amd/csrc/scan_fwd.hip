@@ -29,7 +29,10 @@
 
 namespace ssm {
 
-template <typename IO, int N, int NPL, int CPW, int T, int PD>
+// MODE 0: full forward (y, chunk states, final state).  MODE 1: first phase of
+// a sequence split: the segment's end state from a zero start, and the sum of
+// its step sizes (no y).  blockIdx.z is the segment.
+template <typename IO, int N, int NPL, int CPW, int T, int PD, int MODE>
 __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs a) {
   constexpr int NG = 64 / CPW;             // state groups per wave (lanes = CPW channels x NG groups)
   constexpr int NW = N / (NPL * NG);       // waves per workgroup
@@ -59,9 +62,13 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
   const int64_t b = blockIdx.y;
   const int64_t d0 = (int64_t)blockIdx.x * CPW;
   const int64_t row0 = b * L;
-  const int64_t nck = (L + T - 1) / T;
+  const int64_t seg = blockIdx.z;
+  const int64_t nseg = a.seg_len ? (L + a.seg_len - 1) / a.seg_len : 1;  // (phase 1 runs nseg-1 of them)
+  const int64_t tb = a.seg_len ? seg * a.seg_len : 0;                           // first step
+  const int64_t te = a.seg_len ? (tb + a.seg_len < L ? tb + a.seg_len : L) : L;  // end (exclusive)
+  const int64_t nck = (te - tb + T - 1) / T;
   const int64_t K = (L + kChunkLen - 1) / kChunkLen;
-  const bool has_z = a.z != nullptr;
+  const bool has_z = MODE == 0 && a.z != nullptr;
   const bool sp = a.softplus != 0;
 
   __shared__ __attribute__((aligned(16))) float2 P[T][CPW];         // (dt, dt*u) per step and channel
@@ -92,11 +99,17 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
   const bool dv = d < D;
   const int64_t dc = dv ? d : D - 1;
   float Ap[NPL], h[NPL];
+  float dsum = 0.0f;  // MODE 1: sum of this channel's step sizes over the segment
 #pragma unroll
   for (int k = 0; k < NPL; ++k) {
     const int n = spi * NPL + k;
     Ap[k] = a.A[dc * N + n] * kLog2e;
-    h[k] = a.h0 ? a.h0[(b * D + dc) * N + n] : 0.0f;
+    if (MODE == 1)
+      h[k] = 0.0f;
+    else if (a.seg_len)
+      h[k] = a.seg_state[((b * nseg + seg) * D + dc) * N + n];
+    else
+      h[k] = a.h0 ? a.h0[(b * D + dc) * N + n] : 0.0f;
   }
 
   raw_t r_raw[PD][IPT], r_u[PD][IPT], r_z[PD][IPT];  // loads in flight
@@ -107,8 +120,8 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
                         float(&rc)[BPT]) {
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
-      const int64_t t = k * T + tl0 + j * (NT / G);
-      const int64_t idx = (row0 + (t < L ? t : L - 1)) * D + dgc;
+      const int64_t t = tb + k * T + tl0 + j * (NT / G);
+      const int64_t idx = (row0 + (t < te ? t : te - 1)) * D + dgc;
       ra[j] = V::load(dl, idx);
       ru[j] = V::load(u, idx);
       if (has_z) rz[j] = V::load(zz, idx);
@@ -117,10 +130,10 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
     for (int j = 0; j < BPT; ++j) {
       const int i = tid + j * NT;
       if (BCN % NT == 0 || i < BCN) {
-        const int64_t t = k * T + i / N;
-        const int64_t idx = (row0 + (t < L ? t : L - 1)) * N + i % N;
+        const int64_t t = tb + k * T + i / N;
+        const int64_t idx = (row0 + (t < te ? t : te - 1)) * N + i % N;
         rb[j] = load_io(Bm, idx);
-        rc[j] = load_io(Cm, idx);
+        if (MODE == 0) rc[j] = load_io(Cm, idx);
       }
     }
   };
@@ -129,7 +142,7 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int tl = tl0 + j * (NT / G);
-      const bool tv = k * T + tl < L;  // steps past the end get dt = 0: no state change
+      const bool tv = tb + k * T + tl < te;  // steps past the end get dt = 0: no state change
       const float4 r = V::cvt(ra[j]), x = V::cvt(ru[j]);
       const float rv[4] = {r.x, r.y, r.z, r.w}, xv[4] = {x.x, x.y, x.z, x.w};
       float dt[4];
@@ -152,7 +165,7 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
       if (BCN % NT == 0 || i < BCN) {
         const int tl = i / N, n = i % N;
         BC[tl][n / NPL][n % NPL] = rb[j];
-        BC[tl][n / NPL][NPL + n % NPL] = rc[j];
+        BC[tl][n / NPL][NPL + n % NPL] = MODE == 0 ? rc[j] : 0.0f;
       }
     }
   };
@@ -160,8 +173,8 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int tl = tl0 + j * (NT / G);
-      const int64_t t = k * T + tl;
-      if (t < L && gv) {
+      const int64_t t = tb + k * T + tl;
+      if (t < te && gv) {
         float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
@@ -180,8 +193,8 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
     }
   };
   auto scan_chunk = [&](int64_t k) {
-    const int64_t t0 = k * T;
-    if (a.chunk_states && (t0 % kChunkLen) == 0 && dv) {
+    const int64_t t0 = tb + k * T;
+    if (MODE == 0 && a.chunk_states && (t0 % kChunkLen) == 0 && dv) {
       float *cs = a.chunk_states + ((b * K + t0 / kChunkLen) * D + d) * N + spi * NPL;
 #pragma unroll
       for (int kk = 0; kk < NPL; ++kk) cs[kk] = h[kk];
@@ -202,9 +215,12 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
       for (int kk = 0; kk < NPL; ++kk) {
         const float da = fast_exp2(p.x * Ap[kk]);
         h[kk] = fmaf(da, h[kk], p.y * bc[kk]);
-        ys = fmaf(bc[NPL + kk], h[kk], ys);
+        if (MODE == 0) ys = fmaf(bc[NPL + kk], h[kk], ys);
       }
-      Y[tl][w][lane] = ys;
+      if (MODE == 0)
+        Y[tl][w][lane] = ys;
+      else
+        dsum += p.x;
     }
   };
 
@@ -224,17 +240,58 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
         if (k + PD < nck) load_chunk(k + PD, r_raw[s], r_u[s], r_z[s], r_b[s], r_c[s]);
         scan_chunk(k);
         __syncthreads();
-        epilogue(k);
+        if (MODE == 0) epilogue(k);
         const int sn = (s + 1) % PD;
         if (k + 1 < nck) prologue(k + 1, r_raw[sn], r_u[sn], r_z[sn], r_b[sn], r_c[sn]);
         __syncthreads();
       }
     }
   }
-  if (a.h_final && dv) {
+  if (MODE == 1) {
+    if (dv) {
+#pragma unroll
+      for (int kk = 0; kk < NPL; ++kk) a.seg_hloc[((b * nseg + seg) * D + d) * N + spi * NPL + kk] = h[kk];
+      if (spi == 0) a.seg_dsum[(b * nseg + seg) * D + d] = dsum;
+    }
+  } else if (a.h_final && dv && seg == nseg - 1) {
 #pragma unroll
     for (int kk = 0; kk < NPL; ++kk) a.h_final[(b * D + d) * N + spi * NPL + kk] = h[kk];
   }
+}
+
+// Second phase of a sequence split: the state entering every segment,
+// h_in[0] = h0, h_in[s+1] = exp(A * sum of dt over s) * h_in[s] + h_loc[s]
+// (composition of the affine maps h -> a h + b of consecutive segments).
+__global__ void __launch_bounds__(256) fwd_seg_combine_kernel(FwdArgs a, int64_t nseg) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b, d, n)
+  if (i >= a.B * a.D * a.N) return;
+  const int64_t n = i % a.N, d = (i / a.N) % a.D, b = i / (a.N * a.D);
+  const float Ap = a.A[d * a.N + n] * kLog2e;
+  float h = a.h0 ? a.h0[i] : 0.0f;
+  for (int64_t s = 0; s < nseg; ++s) {
+    a.seg_state[((b * nseg + s) * a.D + d) * a.N + n] = h;
+    if (s + 1 < nseg)
+      h = fmaf(fast_exp2(Ap * a.seg_dsum[(b * nseg + s) * a.D + d]), h,
+               a.seg_hloc[((b * nseg + s) * a.D + d) * a.N + n]);
+  }
+}
+
+// Sequence split for problems with too few channel tiles to fill the GPU:
+// segments of at least kMinSeg steps, aiming at kSplitTarget workgroups of 32
+// channels.  Depends on sizes only, so the workspace query agrees with it.
+constexpr int64_t kMinSeg = 4096;
+constexpr int64_t kSplitTarget = 512;
+
+static int64_t split_len(int64_t B, int64_t L, int64_t D) {
+  const int64_t tiles64 = B * ((D + 63) / 64);
+  if (tiles64 >= 128 || L < 2 * kMinSeg) return 0;
+  const int64_t tiles32 = B * ((D + 31) / 32);
+  int64_t nseg = (kSplitTarget + tiles32 - 1) / tiles32;
+  if (nseg > L / kMinSeg) nseg = L / kMinSeg;
+  if (nseg < 2) return 0;
+  int64_t len = (L + nseg - 1) / nseg;
+  len = (len + kChunkLen - 1) / kChunkLen * kChunkLen;
+  return len;
 }
 
 // Channels per workgroup (CPW) for dstate N.  A 64-channel tile needs 84 KB
@@ -262,20 +319,41 @@ static int pick_cpw(const FwdArgs &a) {
   constexpr int NPL = N >= 2 ? 2 : 1;
   constexpr int mincpw = 64 * NPL / N > 16 ? 64 * NPL / N : 16;
   if (env == 16 || env == 32 || env == 64) return env < mincpw ? mincpw : env;
+  if (mincpw > 32) return 64;
+  if (split_len(a.B, a.L, a.D)) return 32;  // split sequences use 32-channel tiles
   const int64_t wg64 = a.B * ((a.D + 63) / 64);
-  if (wg64 <= device_cus() || mincpw > 32) return 64;
-  return 32;
+  return wg64 <= device_cus() ? 64 : 32;
 }
 
 template <typename IO, int N, int CPW>
-static hipError_t launch_fwd_cpw(const FwdArgs &a, hipStream_t s) {
+static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   constexpr int NPL = N >= 2 ? 2 : 1;
   constexpr int NW = N * CPW / (64 * NPL);
   constexpr int T = 32;
   constexpr int IPT = T * (CPW / 4) / (64 * NW);
   constexpr int PD = IPT <= 2 ? 2 : 1;
-  dim3 grid((unsigned)((a.D + CPW - 1) / CPW), (unsigned)a.B);
-  hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD>), grid, dim3(64 * NW), 0, s, a);
+  FwdArgs a = a0;
+  a.seg_len = split_len(a.B, a.L, a.D);
+  const unsigned tiles = (unsigned)((a.D + CPW - 1) / CPW);
+  if (a.seg_len == 0) {
+    hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0>), dim3(tiles, (unsigned)a.B, 1), dim3(64 * NW), 0, s, a);
+    return hipGetLastError();
+  }
+  const int64_t nseg = (a.L + a.seg_len - 1) / a.seg_len;
+  float *ws = (float *)a.workspace;
+  a.seg_hloc = ws;
+  a.seg_state = ws + a.B * nseg * a.D * a.N;
+  a.seg_dsum = ws + 2 * a.B * nseg * a.D * a.N;
+  hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 1>), dim3(tiles, (unsigned)a.B, (unsigned)(nseg - 1)),
+                     dim3(64 * NW), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nst = a.B * a.D * a.N;
+  hipLaunchKernelGGL(fwd_seg_combine_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, a, nseg);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0>), dim3(tiles, (unsigned)a.B, (unsigned)nseg),
+                     dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
@@ -305,7 +383,12 @@ static hipError_t launch_fwd_io(const FwdArgs &a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-int64_t fwd_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int) { return 0; }
+int64_t fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int) {
+  const int64_t len = split_len(B, L, D);
+  if (len == 0) return 0;
+  const int64_t nseg = (L + len - 1) / len;
+  return (2 * B * nseg * D * N + B * nseg * D) * 4;
+}
 
 hipError_t launch_fwd(const FwdArgs &a, int io_dtype, hipStream_t s) {
   return io_dtype == 0 ? launch_fwd_io<float>(a, s) : launch_fwd_io<bf16>(a, s);

@@ -131,7 +131,7 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
                 (long long)(workspace ? workspace_bytes : 0));
   ssm::FwdArgs a{batch, seqlen, dim, dstate, u,       delta, Bmat,         Cmat,
                  z,     A,      Dskip, delta_bias, h0, delta_softplus != 0, h_final, y,
-                 chunk_states, workspace, workspace_bytes};
+                 chunk_states, workspace, workspace_bytes, 0, nullptr, nullptr, nullptr};
   return hip_status(ssm::launch_fwd(a, io_dtype, (hipStream_t)hip_stream), "ssm_scan_fwd launch");
 }
 

@@ -110,6 +110,18 @@ def test_fwd_small(ssm, B, L, D, N, dtype):
     _check_fwd(ssm, _problem(B, L, D, N, dtype, seed=B * 1000 + L + N), TOL[dtype])
 
 
+@pytest.mark.parametrize("B,L,D,N,dtype", [
+    (1, 10000, 16, 16, torch.float32), (1, 10000, 16, 16, torch.bfloat16),
+    (2, 9000, 24, 8, torch.float32), (1, 12289, 8, 2, torch.float32)])
+def test_fwd_sequence_split(ssm, B, L, D, N, dtype):
+    """Few channels and a long sequence: the forward splits the sequence into
+    segments (local end states, then their composition, then the scan of each
+    segment from its true initial state)."""
+    lib = ssm.load()
+    assert lib.ssm_scan_fwd_workspace_bytes(B, L, D, N, 0 if dtype == torch.float32 else 1) > 0
+    _check_fwd(ssm, _problem(B, L, D, N, dtype, seed=L % 97, h0=True), TOL[dtype])
+
+
 def test_fwd_workload0(ssm):
     p = workload_inputs(0)
     _check_fwd(ssm, p, TOL[torch.float32])

@@ -84,8 +84,9 @@ const char *ssm_last_error(void);
 int64_t ssm_scan_chunk_len(void);
 
 /* Bytes of the chunk_states buffer: batch * ceil(seqlen/T) * dim * dstate * 4.
- * Layout (B, K, D, N) fp32, K = ceil(seqlen/T); slot k holds the state just
- * before step k*T (slot 0 is h0, or zeros).  Returns -1 on invalid sizes. */
+ * Layout (B, K, N, D) fp32 (channels fastest), K = ceil(seqlen/T); slot k
+ * holds the state just before step k*T (slot 0 is h0, or zeros).  Returns -1
+ * on invalid sizes. */
 int64_t ssm_scan_chunk_states_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 
 /* Device workspace the forward scan needs for these sizes (may be 0; then

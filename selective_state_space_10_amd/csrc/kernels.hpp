@@ -8,8 +8,9 @@
 namespace ssm {
 
 // Steps between two saved chunk-boundary states (the forward writes the state
-// before every multiple of this step; the backward recomputes within chunks).
-constexpr int64_t kChunkLen = 256;
+// before every multiple of this step; the backward recomputes a chunk's
+// states into registers, so a chunk must fit there).
+constexpr int64_t kChunkLen = 32;
 
 struct FwdArgs {
   int64_t B, L, D, N;

@@ -3,180 +3,475 @@
 // Reverse-mode derivative of the recurrence h_t = exp(dt_t A) h_{t-1} +
 // dt_t B_t u_t, y_t = (C_t h_t + D u_t) silu(z_t).  With e_t = dy_t silu(z_t)
 // the adjoint of the state runs backwards in time,
-//   lambda_t = e_t C_t + exp(dt_{t+1} A) lambda_{t+1}   (lambda_{L} = dh_final),
-// and every input gradient is a local product with lambda or e.  States are
-// not read from memory: each chunk of kChunkLen steps is recomputed from the
-// chunk-boundary state the forward saved (reading guide of arXiv 2312.00752,
-// "Donanım Duyarlı Durum Genişletme": intermediate states are recomputed in
-// the backward pass).
+//   lambda_t = e_t C_t + exp(dt_{t+1} A) lambda_{t+1}   (from dh_final at the end),
+// and every input gradient is a local product with lambda, e or the state.
+// States are not read from memory: each chunk of kChunkLen steps is
+// recomputed from the chunk-boundary state the forward saved (reading guide
+// of arXiv 2312.00752, "Donanım Duyarlı Durum Genişletme": intermediate states
+// are recomputed in the backward pass).
 //
-// Mapping: one lane per channel (b, d) holding all N states.  Sums over
-// channels (dB, dC) are reduced across the wave and written as per-tile
-// partials; sums over batch rows (dA, dD, dbias) as per-row partials; a second
-// kernel adds the partials in a fixed order, so results are deterministic.
+// One workgroup owns 64 channels (one per lane) of one batch row and all N
+// states of them: wave w holds states 2w and 2w+1.  Per chunk of 32 steps:
+//   - Prologue (cooperative, 16-byte or 8-byte accesses): dt, dt*u, e, u,
+//     d dt/d raw and dy*silu'(z) per (step, channel) into LDS, and B, C.
+//   - Recompute: the chunk's states and decay factors, forwards, into
+//     registers (32 steps x 2 states x 2 values per lane).
+//   - Reverse sweep in groups of 8 steps.  Each step leaves three per-lane
+//     partial sums over the lane's states in LDS (C h, lambda B, lambda a h A)
+//     and the per-state contributions to dB and dC, which are summed over
+//     channels: once across lane pairs with a DPP exchange (odd lanes keep
+//     their two states in swapped order, so that one add serves both), then
+//     through LDS.
+//   - Epilogue (one (step, channel) item per thread): sums over the waves,
+//     writes du, ddelta and dz, and accumulates dD and d bias.
+// Sums over channel tiles (dB, dC) and over batch rows and sequence segments
+// (dA, dD, d bias) are written as partials and added by small kernels in a
+// fixed order, so results are deterministic.
+//
+// Long sequences with few channels are split into segments like the forward:
+// the adjoint entering a segment from the right is the composition of the
+// later segments' affine maps lambda -> exp(A sum dt) lambda + local part.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace ssm {
 
+namespace {
+
+constexpr int kCPW = 64;  // channels per workgroup (one per lane)
+constexpr int kTE = 8;    // steps per epilogue group
+constexpr int kSwap1 = 0xB1;  // DPP quad_perm(1,0,3,2): value of lane ^ 1
+constexpr int kSwap2 = 0x4E;  // DPP quad_perm(2,3,0,1): value of lane ^ 2
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
 struct BwdWs {
-  float *hist;    // (B, ntiles*64, kChunkLen, N): recomputed states of the current chunk
-  float *partB;   // (B, ntiles, L, N)
-  float *partC;   // (B, ntiles, L, N)
-  float *partA;   // (B, D, N)
-  float *partD;   // (B, D)
-  float *partBias;  // (B, D)
-  int64_t ntiles;
+  float *partB, *partC;     // (B, ntiles, L, N): dB, dC summed over one channel tile
+  float *partA;             // (B, nseg, D, N)
+  float *partD, *partBias;  // (B, nseg, D)
+  float *lamloc, *carry;    // (B, nseg, D, N): sequence split only
+  float *dsum;              // (B, nseg, D)
+  int64_t ntiles, nseg, seg_len;
 };
 
-static inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
-static BwdWs carve_ws(void *base, int64_t B, int64_t L, int64_t D, int64_t N, int64_t *total) {
-  const int64_t nt = (D + 63) / 64;
+// Sequence split: when batch rows x channel tiles cannot fill the GPU, cut the
+// sequence into segments (multiples of 256 steps, at least kMinSeg long)
+// aiming at kTarget workgroups.  Depends on sizes only.
+constexpr int64_t kMinSeg = 2048;
+constexpr int64_t kTarget = 512;
+
+int64_t bwd_split_len(int64_t B, int64_t L, int64_t D) {
+  const int64_t tiles = B * ((D + kCPW - 1) / kCPW);
+  if (tiles >= 192 || L < 2 * kMinSeg) return 0;
+  int64_t nseg = (kTarget + tiles - 1) / tiles;
+  if (nseg > L / kMinSeg) nseg = L / kMinSeg;
+  if (nseg < 2) return 0;
+  int64_t len = (L + nseg - 1) / nseg;
+  len = (len + 255) / 256 * 256;
+  return len;
+}
+
+BwdWs carve_ws(void *base, int64_t B, int64_t L, int64_t D, int64_t N, int64_t *total) {
+  BwdWs w;
+  w.ntiles = (D + kCPW - 1) / kCPW;
+  w.seg_len = bwd_split_len(B, L, D);
+  w.nseg = w.seg_len ? (L + w.seg_len - 1) / w.seg_len : 1;
   char *p = (char *)base;
   int64_t off = 0;
-  BwdWs w;
-  w.ntiles = nt;
   auto take = [&](int64_t bytes) {
     float *r = (float *)(p ? p + off : nullptr);
     off += align256(bytes);
     return r;
   };
-  w.hist = take(B * nt * 64 * kChunkLen * N * 4);
-  w.partB = take(B * nt * L * N * 4);
-  w.partC = take(B * nt * L * N * 4);
-  w.partA = take(B * D * N * 4);
-  w.partD = take(B * D * 4);
-  w.partBias = take(B * D * 4);
+  const int64_t S = w.nseg;
+  w.partB = take(B * w.ntiles * L * N * 4);
+  w.partC = take(B * w.ntiles * L * N * 4);
+  w.partA = take(B * S * D * N * 4);
+  w.partD = take(B * S * D * 4);
+  w.partBias = take(B * S * D * 4);
+  if (w.seg_len) {
+    w.lamloc = take(B * S * D * N * 4);
+    w.carry = take(B * S * D * N * 4);
+    w.dsum = take(B * S * D * 4);
+  } else {
+    w.lamloc = w.carry = w.dsum = nullptr;
+  }
   if (total) *total = off;
   return w;
 }
 
-int64_t bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int) {
-  int64_t total = 0;
-  carve_ws(nullptr, B, L, D, N, &total);
-  return total;
-}
+// MODE 0: full backward of one segment (or of the whole sequence).
+// MODE 1: first phase of a sequence split: the adjoint leaving the segment on
+// the left from a zero adjoint on the right, and the sum of the step sizes;
+// blockIdx.z + 1 is the segment.
+template <typename IO, int N, int MODE>
+__global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs a, BwdWs ws) {
+  constexpr int NPL = N >= 2 ? 2 : 1;  // states per lane
+  constexpr int NW = N / NPL;          // waves (state slices)
+  constexpr int NT = 64 * NW;
+  constexpr int CPW = kCPW;
+  constexpr int T = (int)kChunkLen;
+  constexpr int TE = kTE;
+  constexpr int NTG = T / TE;
+  constexpr int G = CPW / 4;            // 4-channel groups
+  constexpr int IPT = T * G / NT;       // prologue items per thread
+  constexpr int IPE = TE * CPW / NT;    // epilogue items per thread
+  constexpr int BCN = T * N;
+  constexpr int BPT = (BCN + NT - 1) / NT;
+  static_assert(T % TE == 0 && (T * G) % NT == 0 && IPT >= 1 && (TE * CPW) % NT == 0 && IPE >= 1,
+                "work must split evenly over threads");
+  static_assert(NT % G == 0, "a thread's channel group must not change between items");
+  using V = Vec4<IO>;
+  typedef typename V::raw raw_t;
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
+  const IO *__restrict__ u = (const IO *)a.u;
+  const IO *__restrict__ dl = (const IO *)a.delta;
+  const IO *__restrict__ zz = (const IO *)a.z;
+  const IO *__restrict__ dyp = (const IO *)a.dy;
+  const IO *__restrict__ Bm = (const IO *)a.Bm;
+  const IO *__restrict__ Cm = (const IO *)a.Cm;
 
-template <typename IO, int N>
-__global__ void __launch_bounds__(64) bwd_channel_kernel(BwdArgs a, BwdWs ws) {
-  const IO *u = (const IO *)a.u, *dl = (const IO *)a.delta, *zz = (const IO *)a.z;
-  const IO *dy = (const IO *)a.dy, *Bm = (const IO *)a.Bm, *Cm = (const IO *)a.Cm;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int par = NPL == 2 ? (lane & 1) : 0;  // odd lanes keep their two states swapped
   const int64_t L = a.L, D = a.D;
-  const int64_t b = blockIdx.y, tile = blockIdx.x;
-  const int64_t d = tile * 64 + lane;
+  const int64_t tile = blockIdx.x, b = blockIdx.y;
+  const int64_t seg = MODE == 1 ? (int64_t)blockIdx.z + 1 : (int64_t)blockIdx.z;
+  const int64_t nseg = ws.nseg;
+  const int64_t tb = ws.seg_len ? seg * ws.seg_len : 0;
+  const int64_t te = ws.seg_len ? (tb + ws.seg_len < L ? tb + ws.seg_len : L) : L;
+  const int64_t nck = (te - tb + T - 1) / T;
+  const int64_t K = (L + T - 1) / T;
+  const int64_t d0 = tile * CPW;
+  const int64_t row0 = b * L;
+  const bool has_z = a.z != nullptr;
+  const bool sp = a.softplus != 0;
+
+  __shared__ __attribute__((aligned(16))) float2 P[T][CPW];  // (dt, dt*u)
+  __shared__ __attribute__((aligned(16))) float E[T][CPW];   // dy * silu(z)
+  __shared__ __attribute__((aligned(16))) float U[T][CPW];   // u
+  __shared__ __attribute__((aligned(16))) float SG[T][CPW];  // d dt / d raw delta
+  __shared__ __attribute__((aligned(16))) float GZ[T][CPW];  // dy * silu'(z)
+  __shared__ __attribute__((aligned(16))) float BCs[2][T][NW][4];  // B, C in the slot order of each lane parity
+  __shared__ __attribute__((aligned(16))) float Q[3][TE][NW][64];  // per-lane partials: C h, lambda B, r A
+  __shared__ __attribute__((aligned(16))) float X[NW][TE][4][32];  // channel-sum staging of dB, dC
+
+  // --- prologue ownership: channel group g, steps tl0 + j*(NT/G)
+  const int g = tid % G;
+  const int tl0 = tid / G;
+  const int64_t dg = d0 + 4 * g;
+  const bool gv = dg < D;  // D % 4 == 0: a group is all valid or all not
+  const int64_t dgc = gv ? dg : D - 4;
+  float bias4[4] = {0.f, 0.f, 0.f, 0.f};
+  if (a.bias) {
+    const float4 v = *(const float4 *)(a.bias + dgc);
+    bias4[0] = v.x, bias4[1] = v.y, bias4[2] = v.z, bias4[3] = v.w;
+  }
+
+  // --- sweep ownership: channel d0 + lane, slot s holds state w*NPL + (s ^ par)
+  const int64_t d = d0 + lane;
   const bool dv = d < D;
   const int64_t dc = dv ? d : D - 1;
-  const bool sp = a.softplus != 0;
-  const float bias = a.bias ? a.bias[dc] : 0.0f;
-  const float Dv = a.Dskip ? a.Dskip[dc] : 0.0f;
-  const int64_t K = (L + kChunkLen - 1) / kChunkLen;
-  float An[N], Ap[N], lam[N], dAacc[N], hst[N], h[N];
+  const float Dv = (MODE == 0 && a.Dskip) ? a.Dskip[dc] : 0.0f;
+  int nst[NPL];
+  float Ap[NPL], An[NPL], lam[NPL], dAacc[NPL];
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
-    An[n] = a.A[dc * N + n];
-    Ap[n] = An[n] * kLog2e;
-    lam[n] = (a.dh_final && dv) ? a.dh_final[(b * D + dc) * N + n] : 0.0f;
-    dAacc[n] = 0.0f;
+  for (int s = 0; s < NPL; ++s) {
+    nst[s] = w * NPL + (s ^ par);
+    An[s] = a.A[dc * N + nst[s]];
+    Ap[s] = An[s] * kLog2e;
+    dAacc[s] = 0.0f;
+    float l0 = 0.0f;
+    if (MODE == 0) {
+      if (ws.seg_len)
+        l0 = ws.carry[((b * nseg + seg) * D + dc) * N + nst[s]];
+      else if (a.dh_final)
+        l0 = a.dh_final[(b * D + dc) * N + nst[s]];
+    }
+    lam[s] = dv ? l0 : 0.0f;
   }
-  float dD_acc = 0.0f, dbias_acc = 0.0f;
-  float *hs = ws.hist + ((b * ws.ntiles * 64 + d) * kChunkLen) * N;
+  float dD_acc = 0.0f, dbias_acc = 0.0f, dsum = 0.0f;
 
-  for (int64_t kc = K - 1; kc >= 0; --kc) {
-    const int64_t t0 = kc * kChunkLen;
-    const int64_t t1 = (t0 + kChunkLen < L) ? t0 + kChunkLen : L;
+  raw_t r_dl[IPT], r_u[IPT], r_z[IPT], r_dy[IPT];
+  float r_b[BPT], r_c[BPT], r_h[NPL];
+
+  auto load_chunk = [&](int64_t kc) {
+    const int64_t t0 = tb + kc * T;
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-      hst[n] = a.chunk_states[((b * K + kc) * D + dc) * N + n];
-      h[n] = hst[n];
+    for (int j = 0; j < IPT; ++j) {
+      const int64_t t = t0 + tl0 + j * (NT / G);
+      const int64_t idx = (row0 + (t < te ? t : te - 1)) * D + dgc;
+      r_dl[j] = V::load(dl, idx);
+      r_dy[j] = V::load(dyp, idx);
+      if (MODE == 0) r_u[j] = V::load(u, idx);
+      if (has_z) r_z[j] = V::load(zz, idx);
     }
-    for (int64_t t = t0; t < t1; ++t) {
-      const int64_t idx = (b * L + t) * D + dc;
-      const float dt = step_size(load_io(dl, idx), bias, sp);
-      const float dtu = dt * load_io(u, idx);
 #pragma unroll
-      for (int n = 0; n < N; ++n) {
-        h[n] = fmaf(fast_exp2(dt * Ap[n]), h[n], dtu * load_io(Bm, (b * L + t) * N + n));
-        hs[(t - t0) * N + n] = h[n];
+    for (int j = 0; j < BPT; ++j) {
+      const int i = tid + j * NT;
+      if (BCN % NT == 0 || i < BCN) {
+        const int64_t t = t0 + i / N;
+        const int64_t idx = (row0 + (t < te ? t : te - 1)) * N + i % N;
+        if (MODE == 0) r_b[j] = load_io(Bm, idx);
+        r_c[j] = load_io(Cm, idx);
       }
     }
-    for (int64_t t = t1 - 1; t >= t0; --t) {
-      const int64_t idx = (b * L + t) * D + dc;
-      const int64_t bl = (b * L + t) * N;
-      const float s = load_io(dl, idx) + bias;
-      const float dt = sp ? softplus_f(s) : s;
-      const float x = load_io(u, idx);
-      const float dtu = dt * x;
-      const float g = load_io(dy, idx);
-      const float *ht = hs + (t - t0) * N;
-      const float *hp = (t > t0) ? hs + (t - 1 - t0) * N : nullptr;
-      float pre = Dv * x;
+    if (MODE == 0) {
+      const int64_t k = t0 / T;
 #pragma unroll
-      for (int n = 0; n < N; ++n) pre = fmaf(load_io(Cm, bl + n), ht[n], pre);
-      float e = g, dzv = 0.0f;
-      if (a.z) {
-        const float zv = load_io(zz, idx);
-        const float sz = sigmoid_f(zv);
-        e = g * zv * sz;
-        dzv = g * pre * sz * fmaf(zv, 1.0f - sz, 1.0f);
-      }
-      if (!dv) e = 0.0f;
-      float du_acc = 0.0f, ddt = 0.0f;
-      float cB[N], cC[N];
+      for (int s = 0; s < NPL; ++s) r_h[s] = a.chunk_states[((b * K + k) * N + nst[s]) * D + dc];
+    }
+  };
+
+  auto prologue = [&](int64_t kc) {
+    const int64_t t0 = tb + kc * T;
 #pragma unroll
-      for (int n = 0; n < N; ++n) {
-        const float Bv = load_io(Bm, bl + n), Cv = load_io(Cm, bl + n);
-        const float aa = fast_exp2(dt * Ap[n]);
-        const float hprev = hp ? hp[n] : hst[n];
-        const float lt = fmaf(e, Cv, lam[n]);
-        cC[n] = e * ht[n];
-        cB[n] = lt * dtu;
-        du_acc = fmaf(lt, Bv, du_acc);
-        const float r = lt * hprev * aa;
-        ddt = fmaf(r, An[n], ddt);
-        dAacc[n] = fmaf(r, dt, dAacc[n]);
-        lam[n] = aa * lt;
-      }
-      ddt = fmaf(x, du_acc, ddt);
-      const float draw = sp ? ddt * sigmoid_f(s) : ddt;
-      if (dv) {
-        store_io((IO *)a.du, idx, fmaf(Dv, e, dt * du_acc));
-        store_io((IO *)a.ddelta, idx, draw);
-        if (a.z) store_io((IO *)a.dz, idx, dzv);
-        dbias_acc += draw;
-        dD_acc = fmaf(e, x, dD_acc);
-      }
-      const int64_t po = ((b * ws.ntiles + tile) * L + t) * N;
+    for (int j = 0; j < IPT; ++j) {
+      const int tl = tl0 + j * (NT / G);
+      const bool ok = gv && t0 + tl < te;  // padding steps and channels: dt = 0, e = 0
+      const float4 r4 = V::cvt(r_dl[j]), g4 = V::cvt(r_dy[j]);
+      const float4 x4 = MODE == 0 ? V::cvt(r_u[j]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 z4 = has_z ? V::cvt(r_z[j]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float rv[4] = {r4.x, r4.y, r4.z, r4.w}, gv4[4] = {g4.x, g4.y, g4.z, g4.w};
+      const float xv[4] = {x4.x, x4.y, x4.z, x4.w}, zv[4] = {z4.x, z4.y, z4.z, z4.w};
+      float dt[4], e[4], sg[4], gz[4];
 #pragma unroll
-      for (int n = 0; n < N; ++n) {
-        const float vb = wave_sum(cB[n]);
-        const float vc = wave_sum(cC[n]);
-        if (lane == 0) {
-          ws.partB[po + n] = vb;
-          ws.partC[po + n] = vc;
+      for (int q = 0; q < 4; ++q) {
+        const float s = rv[q] + bias4[q];
+        dt[q] = ok ? (sp ? softplus_f(s) : s) : 0.0f;
+        sg[q] = sp ? sigmoid_f(s) : 1.0f;
+        float ev = gv4[q], gzv = 0.0f;
+        if (has_z) {
+          const float sz = sigmoid_f(zv[q]);
+          ev = gv4[q] * zv[q] * sz;
+          gzv = gv4[q] * sz * fmaf(zv[q], 1.0f - sz, 1.0f);
+        }
+        e[q] = ok ? ev : 0.0f;
+        gz[q] = gzv;
+      }
+      float4 *pp = (float4 *)&P[tl][4 * g];
+      pp[0] = make_float4(dt[0], dt[0] * xv[0], dt[1], dt[1] * xv[1]);
+      pp[1] = make_float4(dt[2], dt[2] * xv[2], dt[3], dt[3] * xv[3]);
+      *(float4 *)&E[tl][4 * g] = make_float4(e[0], e[1], e[2], e[3]);
+      if (MODE == 0) {
+        *(float4 *)&U[tl][4 * g] = x4;
+        *(float4 *)&SG[tl][4 * g] = make_float4(sg[0], sg[1], sg[2], sg[3]);
+        *(float4 *)&GZ[tl][4 * g] = make_float4(gz[0], gz[1], gz[2], gz[3]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int i = tid + j * NT;
+      if (BCN % NT == 0 || i < BCN) {
+        const int tl = i / N, n = i % N;
+        const int sl = n / NPL, k = n % NPL;
+        const float bv = MODE == 0 ? r_b[j] : 0.0f;
+#pragma unroll
+        for (int pp = 0; pp < NPL; ++pp) {
+          BCs[pp][tl][sl][k ^ pp] = bv;
+          BCs[pp][tl][sl][NPL + (k ^ pp)] = r_c[j];
         }
       }
     }
+  };
+
+  if (MODE == 1) {
+    // Adjoint carry only: lambda <- exp(dt A) (e C + lambda), backwards.
+    load_chunk(nck - 1);
+    for (int64_t kc = nck - 1; kc >= 0; --kc) {
+      prologue(kc);
+      if (kc > 0) load_chunk(kc - 1);
+      __syncthreads();
+#pragma unroll
+      for (int tl = T - 1; tl >= 0; --tl) {
+        const float dt = P[tl][lane].x;
+        const float e = E[tl][lane];
+        const float4 bc = *(const float4 *)&BCs[par][tl][w][0];
+        const float cv[2] = {NPL == 2 ? bc.z : bc.y, bc.w};
+#pragma unroll
+        for (int s = 0; s < NPL; ++s) {
+          const float lt = fmaf(e, cv[s], lam[s]);
+          lam[s] = fast_exp2(dt * Ap[s]) * lt;
+        }
+        dsum += dt;
+      }
+      __syncthreads();
+    }
+    if (dv) {
+#pragma unroll
+      for (int s = 0; s < NPL; ++s) ws.lamloc[((b * nseg + seg) * D + d) * N + nst[s]] = lam[s];
+      if (w == 0) ws.dsum[(b * nseg + seg) * D + d] = dsum;
+    }
+    return;
   }
+
+  // ---------------------------------------------------------------- MODE 0
+  auto epilogue = [&](int64_t kc, int tg) {
+    const int64_t t0 = tb + kc * T;
+#pragma unroll
+    for (int j = 0; j < IPE; ++j) {
+      const int tq = (tid + j * NT) / CPW;  // channel of every item is the lane
+      const int tl = tg * TE + tq;
+      const int64_t t = t0 + tl;
+      if (t < te && dv) {
+        float pre = 0.0f, dua = 0.0f, dda = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+          pre += Q[0][tq][ww][lane];
+          dua += Q[1][tq][ww][lane];
+          dda += Q[2][tq][ww][lane];
+        }
+        const float x = U[tl][lane], e = E[tl][lane], dt = P[tl][lane].x;
+        const float ddl = fmaf(x, dua, dda) * SG[tl][lane];
+        const int64_t idx = (row0 + t) * D + d;
+        store_io((IO *)a.du, idx, fmaf(Dv, e, dt * dua));
+        store_io((IO *)a.ddelta, idx, ddl);
+        if (has_z) store_io((IO *)a.dz, idx, GZ[tl][lane] * fmaf(Dv, x, pre));
+        dD_acc = fmaf(e, x, dD_acc);
+        dbias_acc += ddl;
+      }
+    }
+  };
+  // dB, dC over this workgroup's channels: lane (o = lane/2, half = lane%2)
+  // adds 16 staged values of output o, then its partner's 16.
+  auto channel_sums = [&](int64_t kc, int tg) {
+    const int64_t t0 = tb + kc * T;
+    const int o = lane >> 1, half = lane & 1;
+    const int tq = o >> 2, q = o & 3;
+    const float4 *src = (const float4 *)&X[w][tq][q][16 * half];
+    const float4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
+    float s = ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w)) +
+              (((v2.x + v2.y) + (v2.z + v2.w)) + ((v3.x + v3.y) + (v3.z + v3.w)));
+    s += dpp_mov<kSwap1>(s);
+    if (NPL == 1) s += dpp_mov<kSwap2>(s);  // planes q and q^1 hold the two halves of the lanes
+    const int64_t t = t0 + tg * TE + tq;
+    if (half == 0 && t < te && (NPL == 2 || (q & 1) == 0)) {
+      const int n = NPL == 2 ? w * 2 + (q & 1) : w;
+      float *dst = q < 2 ? ws.partB : ws.partC;
+      dst[((b * ws.ntiles + tile) * L + t) * N + n] = s;
+    }
+  };
+
+  load_chunk(nck - 1);
+  for (int64_t kc = nck - 1; kc >= 0; --kc) {
+    prologue(kc);
+    float hs[NPL];
+#pragma unroll
+    for (int s = 0; s < NPL; ++s) hs[s] = r_h[s];
+    if (kc > 0) load_chunk(kc - 1);
+    __syncthreads();
+
+    // Recompute the chunk's states and decay factors.
+    float Hh[T][NPL], Ha[T][NPL];
+    {
+      float h[NPL];
+#pragma unroll
+      for (int s = 0; s < NPL; ++s) h[s] = hs[s];
+#pragma unroll
+      for (int tl = 0; tl < T; ++tl) {
+        const float2 p = P[tl][lane];
+        const float4 bc = *(const float4 *)&BCs[par][tl][w][0];
+        const float bv[2] = {bc.x, bc.y};
+#pragma unroll
+        for (int s = 0; s < NPL; ++s) {
+          const float da = fast_exp2(p.x * Ap[s]);
+          h[s] = fmaf(da, h[s], p.y * bv[s]);
+          Hh[tl][s] = h[s];
+          Ha[tl][s] = da;
+        }
+      }
+    }
+
+#pragma unroll
+    for (int tg = NTG - 1; tg >= 0; --tg) {
+#pragma unroll
+      for (int tq = TE - 1; tq >= 0; --tq) {
+        const int tl = tg * TE + tq;
+        const float2 p = P[tl][lane];
+        const float e = E[tl][lane];
+        const float4 bc = *(const float4 *)&BCs[par][tl][w][0];
+        const float bv[2] = {bc.x, bc.y};
+        const float cv[2] = {NPL == 2 ? bc.z : bc.y, bc.w};
+        float pre = 0.0f, dup = 0.0f, ddp = 0.0f, cB[NPL], cC[NPL];
+#pragma unroll
+        for (int s = 0; s < NPL; ++s) {
+          const float ht = Hh[tl][s];
+          const float hp = tl > 0 ? Hh[tl > 0 ? tl - 1 : 0][s] : hs[s];
+          const float lt = fmaf(e, cv[s], lam[s]);
+          pre = fmaf(cv[s], ht, pre);
+          cC[s] = e * ht;
+          cB[s] = lt * p.y;
+          dup = fmaf(lt, bv[s], dup);
+          lam[s] = Ha[tl][s] * lt;
+          const float r = lam[s] * hp;
+          ddp = fmaf(r, An[s], ddp);
+          dAacc[s] = fmaf(r, p.x, dAacc[s]);
+        }
+        Q[0][tq][w][lane] = pre;
+        Q[1][tq][w][lane] = dup;
+        Q[2][tq][w][lane] = ddp;
+        if constexpr (NPL == 2) {
+          X[w][tq][par][lane >> 1] = cB[0] + dpp_mov<kSwap1>(cB[1]);
+          X[w][tq][2 + par][lane >> 1] = cC[0] + dpp_mov<kSwap1>(cC[1]);
+        } else {
+          X[w][tq][lane >> 5][lane & 31] = cB[0];
+          X[w][tq][2 + (lane >> 5)][lane & 31] = cC[0];
+        }
+      }
+      __syncthreads();
+      epilogue(kc, tg);
+      channel_sums(kc, tg);
+      __syncthreads();
+    }
+  }
+
   if (dv) {
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-      if (a.dh0) a.dh0[(b * D + d) * N + n] = lam[n];
-      ws.partA[(b * D + d) * N + n] = dAacc[n];
+    for (int s = 0; s < NPL; ++s) {
+      ws.partA[((b * nseg + seg) * D + d) * N + nst[s]] = dAacc[s];
+      if (a.dh0 && seg == 0) a.dh0[(b * D + d) * N + nst[s]] = lam[s];
     }
-    ws.partD[b * D + d] = dD_acc;
-    ws.partBias[b * D + d] = dbias_acc;
+  }
+  // dD and d bias of channel `lane`: one partial per thread, summed over waves.
+  Q[0][0][w][lane] = dD_acc;
+  Q[1][0][w][lane] = dbias_acc;
+  __syncthreads();
+  if (w == 0 && dv) {
+    float sd = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      sd += Q[0][0][ww][lane];
+      sb += Q[1][0][ww][lane];
+    }
+    ws.partD[(b * nseg + seg) * D + d] = sd;
+    ws.partBias[(b * nseg + seg) * D + d] = sb;
   }
 }
 
-// dB, dC: sum the per-tile partials (fixed tile order), cast to the io type.
+// Second phase of a sequence split: the adjoint entering every segment from
+// the right, carry[S-1] = dh_final, carry[s-1] = exp(A sum dt over s) carry[s]
+// + lamloc[s].
+__global__ void __launch_bounds__(256) bwd_seg_combine_kernel(BwdArgs a, BwdWs ws) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b, d, n)
+  if (i >= a.B * a.D * a.N) return;
+  const int64_t n = i % a.N, d = (i / a.N) % a.D, b = i / (a.N * a.D);
+  const int64_t S = ws.nseg;
+  const float Ap = a.A[d * a.N + n] * kLog2e;
+  float c = a.dh_final ? a.dh_final[i] : 0.0f;
+  for (int64_t s = S - 1; s >= 0; --s) {
+    ws.carry[((b * S + s) * a.D + d) * a.N + n] = c;
+    if (s > 0)
+      c = fmaf(fast_exp2(Ap * ws.dsum[(b * S + s) * a.D + d]), c, ws.lamloc[((b * S + s) * a.D + d) * a.N + n]);
+  }
+}
+
+// dB, dC: sum of the per-tile partials in tile order, stored in the io type.
 template <typename IO>
 __global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(BwdArgs a, BwdWs ws) {
   const int64_t LN = a.L * a.N;
@@ -193,20 +488,21 @@ __global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(BwdArgs a, BwdWs ws)
   }
 }
 
-// dA, dD, dbias: sum the per-row partials over batch rows.
+// dA, dD, d bias: sum of the partials over batch rows and segments.
 __global__ void __launch_bounds__(256) bwd_reduce_params_kernel(BwdArgs a, BwdWs ws) {
   const int64_t DN = a.D * a.N;
+  const int64_t R = a.B * ws.nseg;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < DN) {
     float s = 0.0f;
-    for (int64_t b = 0; b < a.B; ++b) s += ws.partA[b * DN + i];
+    for (int64_t r = 0; r < R; ++r) s += ws.partA[r * DN + i];
     a.dA[i] = s;
   }
   if (i < a.D) {
     float sd = 0.0f, sb = 0.0f;
-    for (int64_t b = 0; b < a.B; ++b) {
-      sd += ws.partD[b * a.D + i];
-      sb += ws.partBias[b * a.D + i];
+    for (int64_t r = 0; r < R; ++r) {
+      sd += ws.partD[r * a.D + i];
+      sb += ws.partBias[r * a.D + i];
     }
     if (a.dD) a.dD[i] = sd;
     if (a.dbias) a.dbias[i] = sb;
@@ -214,23 +510,32 @@ __global__ void __launch_bounds__(256) bwd_reduce_params_kernel(BwdArgs a, BwdWs
 }
 
 template <typename IO, int N>
-static hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
+hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
+  constexpr int NT = 64 * (N >= 2 ? N / 2 : 1);
   BwdWs ws = carve_ws(a.workspace, a.B, a.L, a.D, a.N, nullptr);
-  hipLaunchKernelGGL((bwd_channel_kernel<IO, N>), dim3((unsigned)ws.ntiles, (unsigned)a.B), dim3(64), 0, s, a, ws);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const unsigned tiles = (unsigned)ws.ntiles;
+  hipError_t e;
+  if (ws.seg_len) {
+    hipLaunchKernelGGL((bwd_kernel<IO, N, 1>), dim3(tiles, (unsigned)a.B, (unsigned)(ws.nseg - 1)), dim3(NT), 0, s,
+                       a, ws);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t nst = a.B * a.D * a.N;
+    hipLaunchKernelGGL(bwd_seg_combine_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, a, ws);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((bwd_kernel<IO, N, 0>), dim3(tiles, (unsigned)a.B, (unsigned)ws.nseg), dim3(NT), 0, s, a, ws);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t total = a.B * a.L * a.N;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL((bwd_reduce_bc_kernel<IO>), dim3((unsigned)blocks), dim3(256), 0, s, a, ws);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3((unsigned)((a.D * a.N + 255) / 256)), dim3(256), 0, s, a, ws);
   return hipGetLastError();
 }
 
 template <typename IO>
-static hipError_t launch_bwd_io(const BwdArgs &a, hipStream_t s) {
+hipError_t launch_bwd_io(const BwdArgs &a, hipStream_t s) {
   switch (a.N) {
     case 1: return launch_bwd_t<IO, 1>(a, s);
     case 2: return launch_bwd_t<IO, 2>(a, s);
@@ -239,6 +544,14 @@ static hipError_t launch_bwd_io(const BwdArgs &a, hipStream_t s) {
     case 16: return launch_bwd_t<IO, 16>(a, s);
   }
   return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int64_t bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int) {
+  int64_t total = 0;
+  carve_ws(nullptr, B, L, D, N, &total);
+  return total;
 }
 
 hipError_t launch_bwd(const BwdArgs &a, int io_dtype, hipStream_t s) {

@@ -44,6 +44,7 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
   constexpr int BPT = (BCN + NT - 1) / NT;
   static_assert(NW >= 1 && NSP == NW * NG, "states must split evenly over lanes and waves");
   static_assert((T * G) % NT == 0 && IPT >= 1, "items must split evenly over threads");
+  static_assert(kChunkLen % T == 0, "chunk boundaries must fall on chunk starts");
   static_assert(NT % G == 0, "a thread's channel group must not change between items");
   using V = Vec4<IO>;
   typedef typename V::raw raw_t;
@@ -195,9 +196,10 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
   auto scan_chunk = [&](int64_t k) {
     const int64_t t0 = tb + k * T;
     if (MODE == 0 && a.chunk_states && (t0 % kChunkLen) == 0 && dv) {
-      float *cs = a.chunk_states + ((b * K + t0 / kChunkLen) * D + d) * N + spi * NPL;
+      // layout (B, K, N, D): the lanes of a wave write consecutive channels
+      float *cs = a.chunk_states + ((b * K + t0 / kChunkLen) * N + spi * NPL) * D + d;
 #pragma unroll
-      for (int kk = 0; kk < NPL; ++kk) cs[kk] = h[kk];
+      for (int kk = 0; kk < NPL; ++kk) cs[kk * D] = h[kk];
     }
 #pragma unroll
     for (int tl = 0; tl < T; ++tl) {

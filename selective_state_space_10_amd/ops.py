@@ -73,7 +73,8 @@ def _check_common(u, delta, A, B, C, D, z, delta_bias, h0):
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, h0=None,
              return_final_state=False, save_chunk_states=False):
-    """Forward selective scan.  Returns (y, h_final or None, chunk_states or None)."""
+    """Forward selective scan.  Returns (y, h_final or None, chunk_states or None);
+    chunk_states is (batch, K, dstate, dim) with K = ceil(seqlen / chunk_len())."""
     Bsz, L, Dm, N = _check_common(u, delta, A, B, C, D, z, delta_bias, h0)
     lib = _lib.load()
     io = _io_code(u)
@@ -83,7 +84,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
     cs = None
     if save_chunk_states:
         K = -(-L // chunk_len())
-        cs = torch.empty((Bsz, K, Dm, N), dtype=torch.float32, device=dev)
+        cs = torch.empty((Bsz, K, N, Dm), dtype=torch.float32, device=dev)
     wsb = int(lib.ssm_scan_fwd_workspace_bytes(Bsz, L, Dm, N, io))
     if wsb < 0:
         raise ValueError("invalid sizes for the forward workspace query")
@@ -104,7 +105,7 @@ def scan_bwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, chunk_stat
     io = _io_code(u)
     dev = u.device
     K = -(-L // chunk_len())
-    _need("chunk_states", chunk_states, (Bsz, K, Dm, N), torch.float32, dev)
+    _need("chunk_states", chunk_states, (Bsz, K, N, Dm), torch.float32, dev)
     _need("dy", dy, (Bsz, L, Dm), u.dtype, dev)
     _need("dh_final", dh_final, (Bsz, Dm, N), torch.float32, dev, optional=True)
     f32 = dict(dtype=torch.float32, device=dev)

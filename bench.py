@@ -39,6 +39,8 @@ def _parse():
                              "million-length-fwd", "million-length-bwd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=3, help="input sets rotated between steps")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -90,18 +92,39 @@ def _time_launches(fn, steps, warmup, rotate_inputs):
     return start.elapsed_time(stop) / steps, sum(per) / len(per), wall
 
 
-def _cpu_baseline_fwd(p_cpu, sample_desc):
+def _cpu_baseline_fwd(p_cpu, min_seconds=10.0):
+    """The fp64 C oracle's forward over the same inputs, on all host cores it may
+    use, repeated until at least ``min_seconds`` of wall time have passed."""
     from oracle import oracle_c
     threads = oracle_c.default_threads()
     kw = {k: p_cpu[k] for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
-    import numpy as np  # noqa: F401
     conv = {k: oracle_c._f64(v) for k, v in kw.items()}
-    t0 = time.perf_counter()
-    oracle_c.scan_fwd(**conv, delta_softplus=True, nthreads=threads)
-    dt = time.perf_counter() - t0
+    reps, total = 0, 0.0
+    while total < min_seconds:
+        t0 = time.perf_counter()
+        oracle_c.scan_fwd(**conv, delta_softplus=True, nthreads=threads)
+        total += time.perf_counter() - t0
+        reps += 1
     Bsz, L, D = p_cpu["u"].shape
-    return {"value": Bsz * L * D / dt, "unit": UNIT, "cores": threads, "kind": "oracle",
-            "sample": sample_desc, "seconds": round(dt, 3)}
+    N = p_cpu["A"].shape[1]
+    return {"value": reps * Bsz * L * D / total, "unit": UNIT, "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full forward steps of the same workload ({Bsz}x{L}x{D}x{N}, "
+                      f"fp64 C oracle, inputs upcast from the fp32 draws), {total:.1f} s wall",
+            "seconds": round(total, 3)}
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for scaling the HBM byte counters:
+    each launch reads and writes ``nbytes``."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"calibration": "copy", "bytes_read_per_launch": nbytes,
+            "bytes_written_per_launch": nbytes, "launches": reps}
 
 
 def bench_fwd(args, idx, name):
@@ -144,8 +167,7 @@ def bench_fwd(args, idx, name):
     if not args.no_cpu_baseline and idx == 1:
         pc = workload_inputs(idx, device="cuda", seed=idx)
         pc = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in pc.items()}
-        line["cpu_baseline"] = _cpu_baseline_fwd(
-            pc, f"one full step ({Bsz}x{L}x{D}x{N}) of the fp64 C oracle, forward")
+        line["cpu_baseline"] = _cpu_baseline_fwd(pc)
     return line
 
 
@@ -220,6 +242,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration()), flush=True)
+        return
     import selective_state_space_10_amd as m
     m.load()
     if args.workload == "mamba-370m-layer-fwd":

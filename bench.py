@@ -4,7 +4,10 @@ Default: the forward scan at the Mamba-370m layer shape (batch 8, length 2048,
 2048 channels, 16 states, fp32, outputs y and the final state).  One step is
 one forward pass over one batch of synthetic inputs already resident in HBM;
 three input sets are rotated so that the 256 MB last-level cache cannot hold a
-step's inputs.  Prints ONE JSON line (rank 0).
+step's inputs.  Before the W warmup steps the step runs untimed for about 0.25 s
+so that the GPU has left its idle clock state (the count is reported as
+``config.prewarm_steps``); then exactly K steps are timed.  Prints ONE JSON
+line (rank 0).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
@@ -66,11 +69,29 @@ def _traffic(kernel_key: str, sha: str, launches_per_step: int = 1):
     return rec.get("bytes_per_launch")
 
 
+PREWARM_S = 0.25  # untimed seconds of the same step before the warmup steps
+
+
+def _prewarm(fn, rotate_inputs, seconds=PREWARM_S):
+    """Run the step untimed for about ``seconds`` so that the GPU has left its
+    idle clock state before anything is timed; returns the number of steps."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for _ in range(4):
+            fn(rotate_inputs[n % len(rotate_inputs)])
+            n += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
+
 def _time_launches(fn, steps, warmup, rotate_inputs):
     """Per-launch HIP-event durations on the launch stream, plus the wall time
     of the whole timed region (both synchronised on both sides)."""
     import torch
     stream = torch.cuda.current_stream()
+    _time_launches.prewarm_steps = _prewarm(fn, rotate_inputs)
     for i in range(warmup):
         fn(rotate_inputs[i % len(rotate_inputs)])
     torch.cuda.synchronize()
@@ -158,7 +179,8 @@ def bench_fwd(args, idx, name):
                 f"{args.rotate} resident sets)",
         "config": {"workload": name, "batch": Bsz, "seqlen": L, "dim": D, "dstate": N,
                    "io_dtype": str(w.io_dtype).replace("torch.", ""), "outputs": list(w.outputs),
-                   "gpu": torch.cuda.get_device_name(), "wall_s": round(wall, 4)},
+                   "gpu": torch.cuda.get_device_name(), "wall_s": round(wall, 4),
+                   "prewarm_steps": _time_launches.prewarm_steps},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": nbytes,
@@ -194,7 +216,8 @@ def bench_decode(args):
             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16 storage, f32 compute",
             "data": "synthetic", "config": {"workload": "decode-state-update", "batch": w.batch,
-                                            "dim": w.dim, "dstate": w.dstate},
+                                            "dim": w.dim, "dstate": w.dstate,
+                                            "prewarm_steps": _time_launches.prewarm_steps},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                          "algorithmic_bytes": nbytes, "kernel_ms": ms_launch}}
@@ -226,7 +249,8 @@ def bench_bwd(args):
             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16 storage, f32 compute",
             "data": "synthetic", "config": {"workload": "million-length-bwd", "batch": Bsz,
-                                            "seqlen": L, "dim": D, "dstate": N},
+                                            "seqlen": L, "dim": D, "dstate": N,
+                                            "prewarm_steps": _time_launches.prewarm_steps},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                          "algorithmic_bytes": nbytes, "kernel_ms": ms_launch}}

@@ -201,28 +201,45 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
 #pragma unroll
       for (int kk = 0; kk < NPL; ++kk) cs[kk * D] = h[kk];
     }
+    // LDS reads run one sub-block of SB steps ahead of their use.
+    constexpr int SB = 4;
+    float2 pv[2][SB];
+    float bcv[2][SB][2 * NPL];
+    auto read_sub = [&](int j, float2(&pd)[SB], float(&bd)[SB][2 * NPL]) {
 #pragma unroll
-    for (int tl = 0; tl < T; ++tl) {
-      const float2 p = P[tl][c];
-      float bc[2 * NPL];
-      if constexpr (NPL == 2) {
-        const float4 q = *(const float4 *)&BC[tl][spi][0];
-        bc[0] = q.x, bc[1] = q.y, bc[2] = q.z, bc[3] = q.w;
-      } else {
+      for (int q = 0; q < SB; ++q) {
+        const int tl = j * SB + q;
+        pd[q] = P[tl][c];
+        if constexpr (NPL == 2) {
+          const float4 v = *(const float4 *)&BC[tl][spi][0];
+          bd[q][0] = v.x, bd[q][1] = v.y, bd[q][2] = v.z, bd[q][3] = v.w;
+        } else {
 #pragma unroll
-        for (int q = 0; q < 2 * NPL; ++q) bc[q] = BC[tl][spi][q];
+          for (int r = 0; r < 2 * NPL; ++r) bd[q][r] = BC[tl][spi][r];
+        }
       }
-      float ys = 0.0f;
+    };
+    read_sub(0, pv[0], bcv[0]);
 #pragma unroll
-      for (int kk = 0; kk < NPL; ++kk) {
-        const float da = fast_exp2(p.x * Ap[kk]);
-        h[kk] = fmaf(da, h[kk], p.y * bc[kk]);
-        if (MODE == 0) ys = fmaf(bc[NPL + kk], h[kk], ys);
+    for (int j = 0; j < T / SB; ++j) {
+      if (j + 1 < T / SB) read_sub(j + 1, pv[(j + 1) & 1], bcv[(j + 1) & 1]);
+#pragma unroll
+      for (int q = 0; q < SB; ++q) {
+        const int tl = j * SB + q;
+        const float2 p = pv[j & 1][q];
+        const float *bc = bcv[j & 1][q];
+        float ys = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < NPL; ++kk) {
+          const float da = fast_exp2(p.x * Ap[kk]);
+          h[kk] = fmaf(da, h[kk], p.y * bc[kk]);
+          if (MODE == 0) ys = fmaf(bc[NPL + kk], h[kk], ys);
+        }
+        if (MODE == 0)
+          Y[tl][w][lane] = ys;
+        else
+          dsum += p.x;
       }
-      if (MODE == 0)
-        Y[tl][w][lane] = ys;
-      else
-        dsum += p.x;
     }
   };
 

@@ -39,14 +39,19 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         P = ctypes.c_void_p
         I = ctypes.c_int64
-        lib.oracle_scan_fwd.argtypes = [I, I, I, I] + [P] * 8 + [ctypes.c_int, P, P, P, I, P,
-                                                                ctypes.c_int]
-        lib.oracle_scan_fwd.restype = ctypes.c_int
-        lib.oracle_scan_bwd.argtypes = [I, I, I, I] + [P] * 8 + [ctypes.c_int, P, P, P] + [P] * 9 \
-            + [ctypes.c_int]
-        lib.oracle_scan_bwd.restype = ctypes.c_int
-        lib.oracle_state_update.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, ctypes.c_int, P]
-        lib.oracle_state_update.restype = ctypes.c_int
+        CI = ctypes.c_int
+        lib.oracle_scan_fwd.argtypes = [I, I, I, I] + [P] * 8 + [CI, P, P, P, I, P, CI]
+        lib.oracle_scan_fwd.restype = CI
+        lib.oracle_scan_fwd_ex.argtypes = lib.oracle_scan_fwd.argtypes + [CI]
+        lib.oracle_scan_fwd_ex.restype = CI
+        lib.oracle_scan_bwd.argtypes = [I, I, I, I] + [P] * 8 + [CI, P, P, P] + [P] * 9 + [CI]
+        lib.oracle_scan_bwd.restype = CI
+        lib.oracle_scan_bwd_ex.argtypes = lib.oracle_scan_bwd.argtypes + [CI]
+        lib.oracle_scan_bwd_ex.restype = CI
+        lib.oracle_state_update.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, CI, P]
+        lib.oracle_state_update.restype = CI
+        lib.oracle_state_update_ex.argtypes = lib.oracle_state_update.argtypes + [CI]
+        lib.oracle_state_update_ex.restype = CI
         for f in ("oracle_softplus", "oracle_sigmoid", "oracle_silu"):
             getattr(lib, f).argtypes = [ctypes.c_double]
             getattr(lib, f).restype = ctypes.c_double
@@ -74,9 +79,23 @@ def default_threads() -> int:
         return os.cpu_count() or 1
 
 
+ZOH, REVERSE, DELTA_PER_TOKEN = 1, 2, 4
+
+
+def _flags(zoh, reverse, delta, u):
+    f = (ZOH if zoh else 0) | (REVERSE if reverse else 0)
+    if delta.ndim == 2:  # one raw step size per token, (B, L)
+        if delta.shape != u.shape[:2]:
+            raise ValueError("a per-token delta must be (batch, seqlen)")
+        f |= DELTA_PER_TOKEN
+    return f
+
+
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, h0=None,
-             chunk_len=None, nthreads=None):
-    """Returns (y, h_final, chunk_states or None) in fp64."""
+             chunk_len=None, nthreads=None, zoh=False, reverse=False):
+    """Returns (y, h_final, chunk_states or None) in fp64.  ``zoh``: exact
+    zero-order-hold input term; ``reverse``: scan from the last step to the
+    first; a (batch, seqlen) ``delta`` is one step size per token."""
     u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
     D, z, delta_bias, h0 = map(_f64, (D, z, delta_bias, h0))
     Bsz, L, Dm = u.shape
@@ -87,48 +106,53 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
     if chunk_len:
         K = (L + chunk_len - 1) // chunk_len
         cs = np.empty((Bsz, K, Dm, N))
-    rc = _load().oracle_scan_fwd(Bsz, L, Dm, N, _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D),
-                                 _p(z), _p(delta_bias), int(bool(delta_softplus)), _p(h0), _p(y),
-                                 _p(hf), int(chunk_len or 0), _p(cs),
-                                 int(nthreads or default_threads()))
+    rc = _load().oracle_scan_fwd_ex(Bsz, L, Dm, N, _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D),
+                                    _p(z), _p(delta_bias), int(bool(delta_softplus)), _p(h0), _p(y),
+                                    _p(hf), int(chunk_len or 0), _p(cs),
+                                    int(nthreads or default_threads()),
+                                    _flags(zoh, reverse, delta, u))
     if rc != 0:
         raise ValueError(f"oracle_scan_fwd failed ({rc})")
     return y, hf, cs
 
 
 def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, h0=None,
-             dy=None, dh_final=None, nthreads=None):
-    """Returns a dict of fp64 gradients: du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0."""
+             dy=None, dh_final=None, nthreads=None, zoh=False, reverse=False):
+    """Returns a dict of fp64 gradients: du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0
+    (options as in scan_fwd; ddelta has delta's shape)."""
     u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
     D, z, delta_bias, h0, dy, dh_final = map(_f64, (D, z, delta_bias, h0, dy, dh_final))
     Bsz, L, Dm = u.shape
     N = A.shape[1]
-    out = dict(du=np.empty_like(u), ddelta=np.empty_like(u), dA=np.empty((Dm, N)),
+    out = dict(du=np.empty_like(u), ddelta=np.empty_like(delta), dA=np.empty((Dm, N)),
                dB=np.empty((Bsz, L, N)), dC=np.empty((Bsz, L, N)),
                dD=np.empty(Dm) if D is not None else None,
                dz=np.empty_like(u) if z is not None else None,
                ddelta_bias=np.empty(Dm) if delta_bias is not None else None,
                dh0=np.empty((Bsz, Dm, N)))
-    rc = _load().oracle_scan_bwd(Bsz, L, Dm, N, _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z),
-                                 _p(delta_bias), int(bool(delta_softplus)), _p(h0), _p(dy),
-                                 _p(dh_final), _p(out["du"]), _p(out["ddelta"]), _p(out["dA"]),
-                                 _p(out["dB"]), _p(out["dC"]), _p(out["dD"]), _p(out["dz"]),
-                                 _p(out["ddelta_bias"]), _p(out["dh0"]),
-                                 int(nthreads or default_threads()))
+    rc = _load().oracle_scan_bwd_ex(Bsz, L, Dm, N, _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D),
+                                    _p(z), _p(delta_bias), int(bool(delta_softplus)), _p(h0), _p(dy),
+                                    _p(dh_final), _p(out["du"]), _p(out["ddelta"]), _p(out["dA"]),
+                                    _p(out["dB"]), _p(out["dC"]), _p(out["dD"]), _p(out["dz"]),
+                                    _p(out["ddelta_bias"]), _p(out["dh0"]),
+                                    int(nthreads or default_threads()),
+                                    _flags(zoh, reverse, delta, u))
     if rc != 0:
         raise ValueError(f"oracle_scan_bwd failed ({rc})")
     return out
 
 
-def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True):
+def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                 zoh=False):
     """One decode step. Returns (new_state, y) in fp64; the input is not modified."""
     st = _f64(state).copy()
     u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
     D, z, delta_bias = map(_f64, (D, z, delta_bias))
     Bsz, Dm, N = st.shape
     y = np.empty((Bsz, Dm))
-    rc = _load().oracle_state_update(Bsz, Dm, N, _p(st), _p(u), _p(delta), _p(A), _p(B), _p(C),
-                                     _p(D), _p(z), _p(delta_bias), int(bool(delta_softplus)), _p(y))
+    rc = _load().oracle_state_update_ex(Bsz, Dm, N, _p(st), _p(u), _p(delta), _p(A), _p(B), _p(C),
+                                        _p(D), _p(z), _p(delta_bias), int(bool(delta_softplus)),
+                                        _p(y), ZOH if zoh else 0)
     if rc != 0:
         raise ValueError(f"oracle_state_update failed ({rc})")
     return st, y

@@ -25,29 +25,58 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def _step_sizes(delta, delta_bias, delta_softplus):
+def _step_sizes(delta, delta_bias, delta_softplus, dim):
+    """Step sizes (B,L,D) and their pre-softplus argument; a (B,L) delta is
+    one raw value per token, the same for every channel."""
+    if delta.ndim == 2:
+        delta = np.repeat(delta[:, :, None], dim, axis=2)
     s = delta if delta_bias is None else delta + delta_bias
     return (np.logaddexp(0.0, s) if delta_softplus else s), s
 
 
+def _coef(dt_t, A, zoh):
+    """Input coefficient per (b, d, n) of one step: dt, or expm1(dt A)/A for
+    the exact zero-order hold (dt where A = 0)."""
+    x = dt_t[:, :, None] * A[None]
+    if not zoh:
+        return np.broadcast_to(dt_t[:, :, None], x.shape)
+    safe = np.where(A == 0.0, 1.0, A)[None]
+    return np.where(A[None] == 0.0, dt_t[:, :, None], np.expm1(x) / safe)
+
+
+def _dcoef_dA(dt_t, A):
+    """d/dA of expm1(dt A)/A: dt^2 (x e^x - e^x + 1)/x^2 with x = dt A, by
+    its Taylor series where the closed form loses digits."""
+    dt3 = dt_t[:, :, None]
+    x = dt3 * A[None]
+    series = sum(x ** k * (k + 1) / float(np.prod(np.arange(1, k + 3))) for k in range(9))
+    small = np.abs(x) < 5e-2
+    xs = np.where(small, 1.0, x)
+    closed = (xs * np.exp(xs) - np.expm1(xs)) / (xs * xs)
+    return dt3 * dt3 * np.where(small, series, closed)
+
+
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, h0=None,
-             chunk_len=None, return_states=False):
+             chunk_len=None, return_states=False, zoh=False, reverse=False):
+    """``zoh``: exact zero-order-hold input coefficient; ``reverse``: the scan
+    runs from the last step to the first (states are returned in scan order)."""
     u, delta, A, B, C, D, z, delta_bias, h0 = map(_f64, (u, delta, A, B, C, D, z, delta_bias, h0))
     Bsz, L, Dm = u.shape
     N = A.shape[1]
-    dt, _ = _step_sizes(delta, delta_bias, delta_softplus)
+    dt, _ = _step_sizes(delta, delta_bias, delta_softplus, Dm)
     h = np.zeros((Bsz, Dm, N)) if h0 is None else h0.copy()
     y = np.empty((Bsz, L, Dm))
     states = np.empty((Bsz, L, Dm, N)) if return_states else None
     chunks = []
-    for t in range(L):
-        if chunk_len and t % chunk_len == 0:
+    order = range(L - 1, -1, -1) if reverse else range(L)
+    for k, t in enumerate(order):
+        if chunk_len and k % chunk_len == 0:
             chunks.append(h.copy())
         decay = np.exp(dt[:, t, :, None] * A[None, :, :])
-        inject = dt[:, t, :, None] * u[:, t, :, None] * B[:, t, None, :]
+        inject = _coef(dt[:, t], A, zoh) * u[:, t, :, None] * B[:, t, None, :]
         h = decay * h + inject
         if return_states:
-            states[:, t] = h
+            states[:, k] = h
         y[:, t, :] = np.einsum("bdn,bn->bd", h, C[:, t, :])
     if D is not None:
         y = y + D[None, None, :] * u
@@ -60,15 +89,19 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
 
 
 def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, h0=None,
-             dy=None, dh_final=None):
+             dy=None, dh_final=None, zoh=False, reverse=False):
     u, delta, A, B, C, D, z, delta_bias, h0, dy, dh_final = map(
         _f64, (u, delta, A, B, C, D, z, delta_bias, h0, dy, dh_final))
     Bsz, L, Dm = u.shape
     N = A.shape[1]
-    dt, s = _step_sizes(delta, delta_bias, delta_softplus)
+    per_token = delta.ndim == 2
+    dt, s = _step_sizes(delta, delta_bias, delta_softplus, Dm)
     hinit = np.zeros((Bsz, Dm, N)) if h0 is None else h0
-    _, _, _, H = scan_fwd(u, delta, A, B, C, None, None, delta_bias, delta_softplus, h0,
-                          return_states=True)
+    _, _, _, Hs = scan_fwd(u, delta, A, B, C, None, None, delta_bias, delta_softplus, h0,
+                           return_states=True, zoh=zoh, reverse=reverse)
+    order = list(range(L - 1, -1, -1)) if reverse else list(range(L))
+    H = np.empty_like(Hs)  # states by memory row
+    H[:, order] = Hs
     pre = np.einsum("bldn,bln->bld", H, C)
     if D is not None:
         pre = pre + D * u
@@ -85,31 +118,42 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
     dA = np.zeros((Dm, N))
     dB = np.empty((Bsz, L, N))
     dC = np.empty((Bsz, L, N))
-    for t in range(L - 1, -1, -1):
+    for k in range(L - 1, -1, -1):
+        t = order[k]
         decay = np.exp(dt[:, t, :, None] * A[None])
-        hprev = H[:, t - 1] if t > 0 else hinit
+        cf = _coef(dt[:, t], A, zoh)
+        hprev = Hs[:, k - 1] if k > 0 else hinit
         lam = e[:, t, :, None] * C[:, t, None, :] + lam_next
+        lamBu = lam * B[:, t, None, :] * u[:, t, :, None]
         dC[:, t] = np.einsum("bd,bdn->bn", e[:, t], H[:, t])
-        dB[:, t] = np.einsum("bdn,bd->bn", lam, dt[:, t] * u[:, t])
-        du[:, t] = np.einsum("bdn,bn->bd", lam, B[:, t]) * dt[:, t]
+        dB[:, t] = np.einsum("bdn,bdn->bn", lam, cf * u[:, t, :, None])
+        du[:, t] = np.einsum("bdn,bdn->bd", lam * cf, np.broadcast_to(B[:, t, None, :], lam.shape))
+        dcoef_ddt = decay if zoh else 1.0
         ddt[:, t] = (np.einsum("bdn,bdn->bd", lam, hprev * decay * A[None])
-                     + np.einsum("bdn,bn->bd", lam, B[:, t]) * u[:, t])
+                     + (lamBu * dcoef_ddt).sum(axis=2))
         dA += np.einsum("bdn,bd->dn", lam * hprev * decay, dt[:, t])
+        if zoh:
+            dA += (lamBu * _dcoef_dA(dt[:, t], A)).sum(axis=0)
         lam_next = decay * lam
     if D is not None:
         du = du + D * e
     dD = (e * u).sum(axis=(0, 1)) if D is not None else None
     ddelta = ddt * expit(s) if delta_softplus else ddt
     dbias = ddelta.sum(axis=(0, 1)) if delta_bias is not None else None
+    if per_token:
+        ddelta = ddelta.sum(axis=2)
     return dict(du=du, ddelta=ddelta, dA=dA, dB=dB, dC=dC, dD=dD, dz=dz, ddelta_bias=dbias,
                 dh0=lam_next)
 
 
-def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True):
+def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                 zoh=False):
     state, u, delta, A, B, C, D, z, delta_bias = map(
         _f64, (state, u, delta, A, B, C, D, z, delta_bias))
-    dt, _ = _step_sizes(delta, delta_bias, delta_softplus)
-    new = np.exp(dt[:, :, None] * A[None]) * state + (dt * u)[:, :, None] * B[:, None, :]
+    s = delta if delta_bias is None else delta + delta_bias
+    dt = np.logaddexp(0.0, s) if delta_softplus else s
+    new = (np.exp(dt[:, :, None] * A[None]) * state
+           + _coef(dt, A, zoh) * u[:, :, None] * B[:, None, :])
     y = np.einsum("bdn,bn->bd", new, C)
     if D is not None:
         y = y + D * u

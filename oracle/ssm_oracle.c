@@ -24,6 +24,21 @@
  *     the plain reverse-mode derivative of the recurrence, with every state
  *     of a channel kept in memory).
  *
+ * Options (the flags argument of the *_ex entry points; 0 = the above):
+ *   ORACLE_ZOH (1): the exact zero-order-hold input term of the reading
+ *     guide's "Yöntem" discretisation, Bbar = (dt A)^-1 (exp(dt A) - 1) dt B,
+ *     so the input coefficient is expm1(dt A) / A (= dt when A = 0) instead
+ *     of dt;
+ *   ORACLE_REVERSE (2): the recurrence runs from the last step to the first
+ *     (the backward direction of a bidirectional mixer such as Hydra, listed
+ *     on the zenn.dev reading list); h0 is the state before the last step
+ *     and chunk slot k is the state before scan step k*chunk_len, i.e. before
+ *     time L-1-k*chunk_len;
+ *   ORACLE_DELTA_PER_TOKEN (4): delta is (B,L), one raw step size per token
+ *     shared by every channel (the reading guide's "Seçim Mekanizması (S6)"
+ *     delta equation broadcasts one value per token over D); ddelta is then
+ *     (B,L), the sum over channels.
+ *
  * Everything is fp64.  Channels (b, d) are independent recurrences; threads
  * split the channels and never reorder the arithmetic inside one channel.
  * Reductions over channels (dB, dC, and over (b, t) for dA, dD, dbias) are
@@ -50,8 +65,13 @@ double oracle_sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
 double oracle_silu(double x) { return x * oracle_sigmoid(x); }
 
+#define ORACLE_ZOH 1
+#define ORACLE_REVERSE 2
+#define ORACLE_DELTA_PER_TOKEN 4
+
 typedef struct {
   int64_t B, L, D, N;
+  int flags;
   const double *u, *delta, *A, *Bm, *Cm, *Dskip, *z, *bias, *h0;
   int softplus;
   /* forward outputs */
@@ -61,7 +81,7 @@ typedef struct {
   const double *dy, *dh_final;
   double *du, *ddelta, *dz, *dh0;
   /* per-thread partial sums, [thread][...] */
-  double *dA_part, *dB_part, *dC_part, *dD_part, *dbias_part;
+  double *dA_part, *dB_part, *dC_part, *dD_part, *dbias_part, *ddelta_part;
   int nthreads;
 } job_t;
 
@@ -70,10 +90,36 @@ typedef struct {
   int tid;
 } targ_t;
 
-static double step_size(const job_t *j, int64_t idx, int64_t d, double *s_out) {
-  double s = j->delta[idx] + (j->bias ? j->bias[d] : 0.0);
+/* Memory row of scan step s. */
+static int64_t row_of(const job_t *j, int64_t s) { return (j->flags & ORACLE_REVERSE) ? j->L - 1 - s : s; }
+
+/* Index of the raw step size of (b, t, d). */
+static int64_t delta_index(const job_t *j, int64_t b, int64_t t, int64_t d) {
+  return (j->flags & ORACLE_DELTA_PER_TOKEN) ? b * j->L + t : (b * j->L + t) * j->D + d;
+}
+
+static double step_size(const job_t *j, int64_t b, int64_t t, int64_t d, double *s_out) {
+  double s = j->delta[delta_index(j, b, t, d)] + (j->bias ? j->bias[d] : 0.0);
   if (s_out) *s_out = s;
   return j->softplus ? oracle_softplus(s) : s;
+}
+
+/* Input coefficient: dt (first-order form) or, with ORACLE_ZOH, the exact
+ * zero-order hold expm1(dt A) / A (limit dt as A -> 0). */
+static double in_coef(const job_t *j, double dt, double A) {
+  if (!(j->flags & ORACLE_ZOH)) return dt;
+  return A == 0.0 ? dt : expm1(dt * A) / A;
+}
+
+/* d/dA of expm1(dt A) / A = dt^2 psi(dt A), psi(x) = (x e^x - e^x + 1) / x^2
+ * = sum_k x^k (k+1)/(k+2)!; the series is used where the closed form cancels. */
+static double zoh_dcoef_dA(double dt, double A) {
+  const double x = dt * A;
+  if (fabs(x) < 1e-2) {
+    const double psi = 1.0 / 2 + x * (1.0 / 3 + x * (1.0 / 8 + x * (1.0 / 30 + x * (1.0 / 144 + x * (1.0 / 840 + x / 5760.0)))));
+    return dt * dt * psi;
+  }
+  return (dt * exp(x) - expm1(x) / A) / A;
 }
 
 /* ---- forward ------------------------------------------------------------ */
@@ -82,18 +128,20 @@ static void fwd_channel(const job_t *j, int64_t b, int64_t d, double *h) {
   const int64_t L = j->L, D = j->D, N = j->N;
   for (int64_t n = 0; n < N; ++n) h[n] = j->h0 ? j->h0[(b * D + d) * N + n] : 0.0;
   const int64_t K = j->chunk_states ? (L + j->chunk_len - 1) / j->chunk_len : 0;
-  for (int64_t t = 0; t < L; ++t) {
-    if (j->chunk_states && t % j->chunk_len == 0) {
-      int64_t k = t / j->chunk_len;
+  for (int64_t st = 0; st < L; ++st) { /* scan step st at memory row t */
+    const int64_t t = row_of(j, st);
+    if (j->chunk_states && st % j->chunk_len == 0) {
+      int64_t k = st / j->chunk_len;
       for (int64_t n = 0; n < N; ++n) j->chunk_states[((b * K + k) * D + d) * N + n] = h[n];
     }
     const int64_t idx = (b * L + t) * D + d;
-    const double dt = step_size(j, idx, d, NULL);
+    const double dt = step_size(j, b, t, d, NULL);
     const double x = j->u[idx];
     double acc = 0.0;
     for (int64_t n = 0; n < N; ++n) {
-      const double a = exp(dt * j->A[d * N + n]);
-      h[n] = a * h[n] + dt * j->Bm[(b * L + t) * N + n] * x;
+      const double An = j->A[d * N + n];
+      const double a = exp(dt * An);
+      h[n] = a * h[n] + in_coef(j, dt, An) * j->Bm[(b * L + t) * N + n] * x;
       acc += j->Cm[(b * L + t) * N + n] * h[n];
     }
     if (j->Dskip) acc += j->Dskip[d] * x;
@@ -116,14 +164,17 @@ static void *fwd_worker(void *p) {
 
 static void bwd_channel(const job_t *j, int tid, int64_t b, int64_t d, double *hist, double *lam) {
   const int64_t L = j->L, D = j->D, N = j->N;
-  /* hist[(t+1)*N + n] = h_t, hist[n] = h_{-1} (the initial state). */
+  /* hist[(st+1)*N + n] = state after scan step st, hist[n] = the initial state. */
   for (int64_t n = 0; n < N; ++n) hist[n] = j->h0 ? j->h0[(b * D + d) * N + n] : 0.0;
-  for (int64_t t = 0; t < L; ++t) {
+  for (int64_t st = 0; st < L; ++st) {
+    const int64_t t = row_of(j, st);
     const int64_t idx = (b * L + t) * D + d;
-    const double dt = step_size(j, idx, d, NULL);
+    const double dt = step_size(j, b, t, d, NULL);
     for (int64_t n = 0; n < N; ++n) {
-      const double a = exp(dt * j->A[d * N + n]);
-      hist[(t + 1) * N + n] = a * hist[t * N + n] + dt * j->Bm[(b * L + t) * N + n] * j->u[idx];
+      const double An = j->A[d * N + n];
+      const double a = exp(dt * An);
+      hist[(st + 1) * N + n] =
+          a * hist[st * N + n] + in_coef(j, dt, An) * j->Bm[(b * L + t) * N + n] * j->u[idx];
     }
   }
   double *dA = j->dA_part + (size_t)tid * D * N;
@@ -133,10 +184,12 @@ static void bwd_channel(const job_t *j, int tid, int64_t b, int64_t d, double *h
    * or dLoss/dh_final at the last step. */
   for (int64_t n = 0; n < N; ++n) lam[n] = j->dh_final ? j->dh_final[(b * D + d) * N + n] : 0.0;
   double dDsum = 0.0, dbias_sum = 0.0;
-  for (int64_t t = L - 1; t >= 0; --t) {
+  const int zoh = (j->flags & ORACLE_ZOH) != 0;
+  for (int64_t st = L - 1; st >= 0; --st) {
+    const int64_t t = row_of(j, st);
     const int64_t idx = (b * L + t) * D + d;
     double s;
-    const double dt = step_size(j, idx, d, &s);
+    const double dt = step_size(j, b, t, d, &s);
     const double x = j->u[idx];
     const double g = j->dy[idx];
     double e = g; /* dLoss/d(pre-gate output) */
@@ -144,7 +197,7 @@ static void bwd_channel(const job_t *j, int tid, int64_t b, int64_t d, double *h
       const double zz = j->z[idx];
       const double sz = oracle_sigmoid(zz);
       double pre = 0.0; /* sum_n C h + D u at this step */
-      for (int64_t n = 0; n < N; ++n) pre += j->Cm[(b * L + t) * N + n] * hist[(t + 1) * N + n];
+      for (int64_t n = 0; n < N; ++n) pre += j->Cm[(b * L + t) * N + n] * hist[(st + 1) * N + n];
       if (j->Dskip) pre += j->Dskip[d] * x;
       e = g * zz * sz;
       j->dz[idx] = g * pre * sz * (1.0 + zz * (1.0 - sz));
@@ -154,19 +207,25 @@ static void bwd_channel(const job_t *j, int tid, int64_t b, int64_t d, double *h
     for (int64_t n = 0; n < N; ++n) {
       const double Bv = j->Bm[(b * L + t) * N + n];
       const double Cv = j->Cm[(b * L + t) * N + n];
-      const double a = exp(dt * j->A[d * N + n]);
-      const double hprev = hist[t * N + n];
-      const double lt = e * Cv + lam[n]; /* lambda_t */
-      dC[(b * L + t) * N + n] += e * hist[(t + 1) * N + n];
-      dB[(b * L + t) * N + n] += lt * dt * x;
-      du += lt * dt * Bv;
-      ddt += lt * (hprev * a * j->A[d * N + n] + Bv * x);
-      dA[d * N + n] += lt * hprev * a * dt;
+      const double An = j->A[d * N + n];
+      const double a = exp(dt * An);
+      const double cf = in_coef(j, dt, An);
+      const double hprev = hist[st * N + n];
+      const double lt = e * Cv + lam[n]; /* lambda at this step */
+      dC[(b * L + t) * N + n] += e * hist[(st + 1) * N + n];
+      dB[(b * L + t) * N + n] += lt * cf * x;
+      du += lt * cf * Bv;
+      /* d coef / d dt is 1 (first-order form) or exp(dt A) (zero-order hold) */
+      ddt += lt * (hprev * a * An + Bv * x * (zoh ? a : 1.0));
+      dA[d * N + n] += lt * hprev * a * dt + (zoh ? lt * Bv * x * zoh_dcoef_dA(dt, An) : 0.0);
       lam[n] = a * lt;
     }
     j->du[idx] = du;
     const double draw = j->softplus ? ddt * oracle_sigmoid(s) : ddt;
-    j->ddelta[idx] = draw;
+    if (j->flags & ORACLE_DELTA_PER_TOKEN)
+      j->ddelta_part[(size_t)tid * j->B * L + b * L + t] += draw;
+    else
+      j->ddelta[idx] = draw;
     dbias_sum += draw;
     dDsum += e * x;
   }
@@ -204,17 +263,18 @@ static void run_threads(job_t *j, void *(*fn)(void *)) {
   free(args);
 }
 
-/* Returns 0 on success, -1 on bad sizes. */
-int oracle_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, const double *u, const double *delta,
-                    const double *A, const double *Bm, const double *Cm, const double *Dskip,
-                    const double *z, const double *delta_bias, int softplus, const double *h0,
-                    double *y, double *h_final, int64_t chunk_len, double *chunk_states,
-                    int nthreads) {
+/* Returns 0 on success, -1 on bad sizes or flags. */
+int oracle_scan_fwd_ex(int64_t B, int64_t L, int64_t D, int64_t N, const double *u,
+                       const double *delta, const double *A, const double *Bm, const double *Cm,
+                       const double *Dskip, const double *z, const double *delta_bias, int softplus,
+                       const double *h0, double *y, double *h_final, int64_t chunk_len,
+                       double *chunk_states, int nthreads, int flags) {
   if (B < 1 || L < 1 || D < 1 || N < 1) return -1;
   if (chunk_states && chunk_len < 1) return -1;
+  if (flags & ~(ORACLE_ZOH | ORACLE_REVERSE | ORACLE_DELTA_PER_TOKEN)) return -1;
   job_t j;
   memset(&j, 0, sizeof(j));
-  j.B = B, j.L = L, j.D = D, j.N = N;
+  j.B = B, j.L = L, j.D = D, j.N = N, j.flags = flags;
   j.u = u, j.delta = delta, j.A = A, j.Bm = Bm, j.Cm = Cm, j.Dskip = Dskip, j.z = z;
   j.bias = delta_bias, j.h0 = h0, j.softplus = softplus;
   j.y = y, j.h_final = h_final, j.chunk_states = chunk_states, j.chunk_len = chunk_len;
@@ -223,20 +283,30 @@ int oracle_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, const double *u,
   return 0;
 }
 
+int oracle_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, const double *u, const double *delta,
+                    const double *A, const double *Bm, const double *Cm, const double *Dskip,
+                    const double *z, const double *delta_bias, int softplus, const double *h0,
+                    double *y, double *h_final, int64_t chunk_len, double *chunk_states,
+                    int nthreads) {
+  return oracle_scan_fwd_ex(B, L, D, N, u, delta, A, Bm, Cm, Dskip, z, delta_bias, softplus, h0, y,
+                            h_final, chunk_len, chunk_states, nthreads, 0);
+}
+
 /* Gradients are overwritten.  dz must be non-NULL iff z is; dD/ddelta_bias/dh0
  * may be NULL (not wanted).  Returns 0 on success, -1 on bad sizes, -2 on
  * allocation failure. */
-int oracle_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, const double *u, const double *delta,
-                    const double *A, const double *Bm, const double *Cm, const double *Dskip,
-                    const double *z, const double *delta_bias, int softplus, const double *h0,
-                    const double *dy, const double *dh_final, double *du, double *ddelta,
-                    double *dA, double *dB, double *dC, double *dD, double *dz,
-                    double *ddelta_bias, double *dh0, int nthreads) {
+int oracle_scan_bwd_ex(int64_t B, int64_t L, int64_t D, int64_t N, const double *u,
+                       const double *delta, const double *A, const double *Bm, const double *Cm,
+                       const double *Dskip, const double *z, const double *delta_bias, int softplus,
+                       const double *h0, const double *dy, const double *dh_final, double *du,
+                       double *ddelta, double *dA, double *dB, double *dC, double *dD, double *dz,
+                       double *ddelta_bias, double *dh0, int nthreads, int flags) {
   if (B < 1 || L < 1 || D < 1 || N < 1) return -1;
   if ((z == NULL) != (dz == NULL)) return -1;
+  if (flags & ~(ORACLE_ZOH | ORACLE_REVERSE | ORACLE_DELTA_PER_TOKEN)) return -1;
   job_t j;
   memset(&j, 0, sizeof(j));
-  j.B = B, j.L = L, j.D = D, j.N = N;
+  j.B = B, j.L = L, j.D = D, j.N = N, j.flags = flags;
   j.u = u, j.delta = delta, j.A = A, j.Bm = Bm, j.Cm = Cm, j.Dskip = Dskip, j.z = z;
   j.bias = delta_bias, j.h0 = h0, j.softplus = softplus;
   j.dy = dy, j.dh_final = dh_final, j.du = du, j.ddelta = ddelta, j.dz = dz, j.dh0 = dh0;
@@ -248,8 +318,11 @@ int oracle_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, const double *u,
   j.dC_part = (double *)calloc(T * B * L * N, sizeof(double));
   j.dD_part = (double *)calloc(T * D, sizeof(double));
   j.dbias_part = (double *)calloc(T * D, sizeof(double));
+  const int per_token = (flags & ORACLE_DELTA_PER_TOKEN) != 0;
+  if (per_token) j.ddelta_part = (double *)calloc(T * B * L, sizeof(double));
   int rc = 0;
-  if (!j.dA_part || !j.dB_part || !j.dC_part || !j.dD_part || !j.dbias_part) {
+  if (!j.dA_part || !j.dB_part || !j.dC_part || !j.dD_part || !j.dbias_part ||
+      (per_token && !j.ddelta_part)) {
     rc = -2;
   } else {
     run_threads(&j, bwd_worker);
@@ -277,22 +350,45 @@ int oracle_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, const double *u,
       if (dD) dD[i] = sd;
       if (ddelta_bias) ddelta_bias[i] = sbias;
     }
+    if (per_token) {
+      const size_t nBL = (size_t)B * L;
+      for (size_t i = 0; i < nBL; ++i) {
+        double sd = 0.0;
+        for (size_t k = 0; k < T; ++k) sd += j.ddelta_part[k * nBL + i];
+        ddelta[i] = sd;
+      }
+    }
   }
   free(j.dA_part);
   free(j.dB_part);
   free(j.dC_part);
   free(j.dD_part);
   free(j.dbias_part);
+  free(j.ddelta_part);
   return rc;
+}
+
+int oracle_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, const double *u, const double *delta,
+                    const double *A, const double *Bm, const double *Cm, const double *Dskip,
+                    const double *z, const double *delta_bias, int softplus, const double *h0,
+                    const double *dy, const double *dh_final, double *du, double *ddelta,
+                    double *dA, double *dB, double *dC, double *dD, double *dz,
+                    double *ddelta_bias, double *dh0, int nthreads) {
+  return oracle_scan_bwd_ex(B, L, D, N, u, delta, A, Bm, Cm, Dskip, z, delta_bias, softplus, h0, dy,
+                            dh_final, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0, nthreads, 0);
 }
 
 /* One token of the recurrence, in place on state (B,D,N).  u, delta, z, y are
  * (B,D); Bm, Cm are (B,N).  Same arithmetic as one step of the forward scan. */
-int oracle_state_update(int64_t B, int64_t D, int64_t N, double *state, const double *u,
-                        const double *delta, const double *A, const double *Bm, const double *Cm,
-                        const double *Dskip, const double *z, const double *delta_bias, int softplus,
-                        double *y) {
+int oracle_state_update_ex(int64_t B, int64_t D, int64_t N, double *state, const double *u,
+                           const double *delta, const double *A, const double *Bm, const double *Cm,
+                           const double *Dskip, const double *z, const double *delta_bias,
+                           int softplus, double *y, int flags) {
   if (B < 1 || D < 1 || N < 1) return -1;
+  if (flags & ~ORACLE_ZOH) return -1; /* one token: no direction, delta is (B,D) */
+  job_t j; /* only for in_coef */
+  memset(&j, 0, sizeof(j));
+  j.flags = flags;
   for (int64_t b = 0; b < B; ++b) {
     for (int64_t d = 0; d < D; ++d) {
       const int64_t idx = b * D + d;
@@ -302,7 +398,8 @@ int oracle_state_update(int64_t B, int64_t D, int64_t N, double *state, const do
       double acc = 0.0;
       for (int64_t n = 0; n < N; ++n) {
         double *h = &state[idx * N + n];
-        *h = exp(dt * A[d * N + n]) * *h + dt * Bm[b * N + n] * x;
+        const double An = A[d * N + n];
+        *h = exp(dt * An) * *h + in_coef(&j, dt, An) * Bm[b * N + n] * x;
         acc += Cm[b * N + n] * *h;
       }
       if (Dskip) acc += Dskip[d] * x;
@@ -310,4 +407,12 @@ int oracle_state_update(int64_t B, int64_t D, int64_t N, double *state, const do
     }
   }
   return 0;
+}
+
+int oracle_state_update(int64_t B, int64_t D, int64_t N, double *state, const double *u,
+                        const double *delta, const double *A, const double *Bm, const double *Cm,
+                        const double *Dskip, const double *z, const double *delta_bias, int softplus,
+                        double *y) {
+  return oracle_state_update_ex(B, D, N, state, u, delta, A, Bm, Cm, Dskip, z, delta_bias, softplus, y,
+                                0);
 }

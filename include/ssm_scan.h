@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 1
+#define SSM_SCAN_ABI_VERSION 2
 
 typedef enum ssm_status {
   SSM_OK = 0,
@@ -70,6 +70,33 @@ typedef enum ssm_status {
 
 typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 
+/*
+ * Option bits of the *_ex entry points (0 = the definition above).
+ *
+ * SSM_FLAG_ZOH: the exact zero-order-hold input term of the reading guide's
+ *   "Yöntem" discretisation, Bbar = (dt A)^-1 (exp(dt A) - 1) dt B, so that
+ *   dBu = expm1(dt A) / A * B * u (= dt B u in the limit A -> 0) instead of
+ *   dt * B * u.  Forward, backward and single-token update.
+ * SSM_FLAG_REVERSE: the recurrence runs from the last step to the first,
+ *   h_t = exp(dt_t A) h_{t+1} + dBu_t; h0 is the state before step L-1,
+ *   h_final the state after step 0, and chunk slot k the state before scan
+ *   step k*T (time L-1-k*T).  This is the second direction of a bidirectional
+ *   mixer (Hydra, on the zenn.dev reading list); see SSM_FLAG_ACCUMULATE.
+ *   Forward and backward.
+ * SSM_FLAG_DELTA_PER_TOKEN: delta is (B, L), one raw step size per token
+ *   shared by every channel, plus the per-channel delta_bias (the reading
+ *   guide's "Seçim Mekanizması (S6)" delta equation broadcasts one value over
+ *   D).  ddelta is then (B, L): the sum of the per-channel gradients.
+ *   Forward and backward.
+ * SSM_FLAG_ACCUMULATE: forward only; y += scan output instead of y = scan
+ *   output (y is read, so it must hold valid data).  A forward scan followed
+ *   by a reverse scan with this flag sums both directions.
+ */
+#define SSM_FLAG_ZOH 1
+#define SSM_FLAG_REVERSE 2
+#define SSM_FLAG_DELTA_PER_TOKEN 4
+#define SSM_FLAG_ACCUMULATE 8
+
 /* SSM_SCAN_ABI_VERSION of the built library. */
 int ssm_abi_version(void);
 
@@ -80,7 +107,7 @@ const char *ssm_status_string(int status);
  * pointer stays valid until the next library call on that thread. */
 const char *ssm_last_error(void);
 
-/* Number of time steps T between two saved chunk-boundary states. */
+/* Number of time steps T between two saved chunk-boundary states (32). */
 int64_t ssm_scan_chunk_len(void);
 
 /* Bytes of the chunk_states buffer: batch * ceil(seqlen/T) * dim * dstate * 4.
@@ -115,6 +142,16 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
                  float *chunk_states, void *workspace, int64_t workspace_bytes,
                  void *hip_stream);
 
+/* ssm_scan_fwd with option bits (SSM_FLAG_*; all four apply).  Unknown bits
+ * return SSM_ERR_UNSUPPORTED.  flags = 0 is exactly ssm_scan_fwd.  The
+ * workspace size does not depend on the flags. */
+int ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                    const void *u, const void *delta, const float *A, const void *Bmat,
+                    const void *Cmat, const float *Dskip, const void *z, const float *delta_bias,
+                    int delta_softplus, const float *h0, float *h_final, void *y,
+                    float *chunk_states, void *workspace, int64_t workspace_bytes,
+                    void *hip_stream, int flags);
+
 /* Device workspace ssm_scan_bwd needs for these sizes.  -1 on invalid sizes. */
 int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                                      int io_dtype);
@@ -146,6 +183,19 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
                  float *dD, void *dz, float *ddelta_bias, float *dh0, void *workspace,
                  int64_t workspace_bytes, void *hip_stream);
 
+/* ssm_scan_bwd with option bits: SSM_FLAG_ZOH, SSM_FLAG_REVERSE and
+ * SSM_FLAG_DELTA_PER_TOKEN, which must match the forward that wrote
+ * chunk_states (SSM_FLAG_ACCUMULATE and unknown bits return
+ * SSM_ERR_UNSUPPORTED).  With SSM_FLAG_DELTA_PER_TOKEN, delta and ddelta are
+ * (B, L).  flags = 0 is exactly ssm_scan_bwd. */
+int ssm_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                    const void *u, const void *delta, const float *A, const void *Bmat,
+                    const void *Cmat, const float *Dskip, const void *z, const float *delta_bias,
+                    int delta_softplus, const float *h0, const float *chunk_states, const void *dy,
+                    const float *dh_final, void *du, void *ddelta, float *dA, void *dB, void *dC,
+                    float *dD, void *dz, float *ddelta_bias, float *dh0, void *workspace,
+                    int64_t workspace_bytes, void *hip_stream, int flags);
+
 /*
  * One decode step (reading guide, "Sorular", the question on KV caches: the
  * model keeps a fixed D x N state per layer and advances it one token at a
@@ -158,6 +208,15 @@ int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, f
                      const void *u, const void *delta, const float *A, const void *Bmat,
                      const void *Cmat, const float *Dskip, const void *z,
                      const float *delta_bias, int delta_softplus, void *y, void *hip_stream);
+
+/* ssm_state_update with option bits: only SSM_FLAG_ZOH applies to one token
+ * (other bits return SSM_ERR_UNSUPPORTED).  flags = 0 is exactly
+ * ssm_state_update. */
+int ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, float *state,
+                        const void *u, const void *delta, const float *A, const void *Bmat,
+                        const void *Cmat, const float *Dskip, const void *z,
+                        const float *delta_bias, int delta_softplus, void *y, void *hip_stream,
+                        int flags);
 
 #ifdef __cplusplus
 }

@@ -6,8 +6,8 @@ recomputation from chunk-boundary states, and the single-token decode update
 of the Mamba selective state-space model (Gu & Dao, arXiv 2312.00752).
 """
 from ._lib import EXPORTS, LIB_PATH, SSMError, load  # noqa: F401
-from .ops import (SelectiveScanFn, chunk_len, scan_bwd, scan_fwd, selective_scan,  # noqa: F401
-                  state_update)
+from .ops import (SelectiveScanFn, bidirectional_scan, chunk_len, scan_bwd, scan_fwd,  # noqa: F401
+                  selective_scan, state_update)
 
 __all__ = ["scan_fwd", "scan_bwd", "state_update", "selective_scan", "SelectiveScanFn",
-           "chunk_len", "load", "SSMError"]
+           "bidirectional_scan", "chunk_len", "load", "SSMError"]

@@ -12,7 +12,14 @@ SSM_BF16 = 1
 # every symbol include/ssm_scan.h declares
 EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_error", "ssm_scan_chunk_len",
            "ssm_scan_chunk_states_bytes", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd",
-           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_state_update")
+           "ssm_scan_fwd_ex", "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_ex",
+           "ssm_state_update", "ssm_state_update_ex")
+
+# option bits of the *_ex entry points
+FLAG_ZOH = 1
+FLAG_REVERSE = 2
+FLAG_DELTA_PER_TOKEN = 4
+FLAG_ACCUMULATE = 8
 
 _lib = None
 
@@ -53,6 +60,10 @@ def load() -> ctypes.CDLL:
     lib.ssm_scan_bwd.argtypes = [I64] * 4 + [INT] + [P] * 8 + [INT] + [P] * 14 + [I64, P]
     lib.ssm_state_update.restype = INT
     lib.ssm_state_update.argtypes = [I64] * 3 + [INT] + [P] * 9 + [INT, P, P]
+    for name in ("ssm_scan_fwd", "ssm_scan_bwd", "ssm_state_update"):
+        ex = getattr(lib, name + "_ex")
+        ex.restype = INT
+        ex.argtypes = getattr(lib, name).argtypes + [INT]
     _lib = lib
     return lib
 

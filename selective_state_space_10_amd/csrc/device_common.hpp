@@ -51,6 +51,11 @@ struct Vec4<float> {
   static __device__ __forceinline__ raw load(const float *p, int64_t i) { return *(const float4 *)(p + i); }
   static __device__ __forceinline__ float4 cvt(raw r) { return r; }
   static __device__ __forceinline__ void store(float *p, int64_t i, float4 v) { *(float4 *)(p + i) = v; }
+  // one element, repeated four times
+  static __device__ __forceinline__ raw splat(const float *p, int64_t i) {
+    const float v = p[i];
+    return make_float4(v, v, v, v);
+  }
 };
 template <>
 struct Vec4<bf16> {
@@ -65,6 +70,11 @@ struct Vec4<bf16> {
     o.x = (uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16);
     o.y = (uint32_t)f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16);
     *(uint2 *)(p + i) = o;
+  }
+  static __device__ __forceinline__ raw splat(const bf16 *p, int64_t i) {
+    const uint32_t b = p[i].bits;
+    const uint32_t w = b | (b << 16);
+    return make_uint2(w, w);
   }
 };
 
@@ -88,6 +98,24 @@ __device__ __forceinline__ float softplus_f(float s) {
 __device__ __forceinline__ float sigmoid_f(float x) { return fast_rcp(1.0f + fast_exp2(-x * kLog2e)); }
 
 __device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
+
+// Input coefficient of the exact zero-order hold, expm1(x) / A with x = dt*A,
+// given da = exp(x) and Ainv = 1/A.  For |x| >= 1/4, (da - 1) * Ainv loses at
+// most 2^-24 / (1 - e^-1/4) relative; below that, dt * (e^x - 1)/x by its
+// Taylor polynomial of degree 5 (remainder below x^6/5040 < 5e-8).  A = 0
+// gives x = 0 and so dt.
+__device__ __forceinline__ float zoh_coef(float dt, float x, float da, float Ainv) {
+  const float phi = fmaf(x, fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.0f / 720, 1.0f / 120), 1.0f / 24), 1.0f / 6), 0.5f), 1.0f);
+  return fabsf(x) < 0.25f ? dt * phi : (da - 1.0f) * Ainv;
+}
+
+// d/dA of expm1(dt A)/A = dt^2 psi(x), psi(x) = (x e^x - e^x + 1)/x^2: the
+// Taylor polynomial sum_k x^k (k+1)/(k+2)! up to k = 5 for |x| < 1/4, else
+// (dt da - coef) * Ainv.
+__device__ __forceinline__ float zoh_dcoef_dA(float dt, float x, float da, float coef, float Ainv) {
+  const float psi = fmaf(x, fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.0f / 840, 1.0f / 144), 1.0f / 30), 0.125f), 1.0f / 3), 0.5f);
+  return fabsf(x) < 0.25f ? dt * dt * psi : (dt * da - coef) * Ainv;
+}
 
 // Step size from the raw input: softplus(raw + bias) or raw + bias.
 __device__ __forceinline__ float step_size(float raw, float bias, bool softplus) {

@@ -12,11 +12,18 @@ namespace ssm {
 // states into registers, so a chunk must fit there).
 constexpr int64_t kChunkLen = 32;
 
+// Option bits (the flags argument of the *_ex entry points).
+constexpr int kFlagZoh = 1;           // exact zero-order-hold input term
+constexpr int kFlagReverse = 2;       // scan from the last step to the first
+constexpr int kFlagDeltaPerToken = 4; // delta is (B, L), shared by all channels
+constexpr int kFlagAccumulate = 8;    // forward only: y += result instead of y = result
+
 struct FwdArgs {
   int64_t B, L, D, N;
   const void *u, *delta, *Bm, *Cm, *z;
   const float *A, *Dskip, *bias, *h0;
   int softplus;
+  int flags;
   float *h_final;
   void *y;
   float *chunk_states;
@@ -34,6 +41,7 @@ struct BwdArgs {
   const void *u, *delta, *Bm, *Cm, *z, *dy;
   const float *A, *Dskip, *bias, *h0, *chunk_states, *dh_final;
   int softplus;
+  int flags;
   void *du, *ddelta, *dB, *dC, *dz;
   float *dA, *dD, *dbias, *dh0;
   void *workspace;
@@ -46,6 +54,7 @@ struct DecodeArgs {
   const void *u, *delta, *Bm, *Cm, *z;
   const float *A, *Dskip, *bias;
   int softplus;
+  int flags;
   void *y;
 };
 

@@ -48,8 +48,15 @@ __device__ __forceinline__ float dpp_mov(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
 struct BwdWs {
   float *partB, *partC;     // (B, ntiles, L, N): dB, dC summed over one channel tile
+  float *partTok;           // (B, ntiles, L): per-token ddelta summed over one channel tile
   float *partA;             // (B, nseg, D, N)
   float *partD, *partBias;  // (B, nseg, D)
   float *lamloc, *carry;    // (B, nseg, D, N): sequence split only
@@ -91,6 +98,7 @@ BwdWs carve_ws(void *base, int64_t B, int64_t L, int64_t D, int64_t N, int64_t *
   const int64_t S = w.nseg;
   w.partB = take(B * w.ntiles * L * N * 4);
   w.partC = take(B * w.ntiles * L * N * 4);
+  w.partTok = take(B * w.ntiles * L * 4);
   w.partA = take(B * S * D * N * 4);
   w.partD = take(B * S * D * 4);
   w.partBias = take(B * S * D * 4);
@@ -109,7 +117,11 @@ BwdWs carve_ws(void *base, int64_t B, int64_t L, int64_t D, int64_t N, int64_t *
 // MODE 1: first phase of a sequence split: the adjoint leaving the segment on
 // the left from a zero adjoint on the right, and the sum of the step sizes;
 // blockIdx.z + 1 is the segment.
-template <typename IO, int N, int MODE>
+// ZOH: the exact zero-order-hold input term coef = expm1(dt A)/A, whose
+// derivatives are d coef/d dt = exp(dt A) and d coef/d A = dt^2 psi(dt A).
+// Reverse direction and one step size per token are runtime flags; steps are
+// numbered in scan order and mapped to memory rows.
+template <typename IO, int N, int MODE, bool ZOH>
 __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs a, BwdWs ws) {
   constexpr int NPL = N >= 2 ? 2 : 1;  // states per lane
   constexpr int NW = N / NPL;          // waves (state slices)
@@ -152,8 +164,11 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
   const int64_t row0 = b * L;
   const bool has_z = a.z != nullptr;
   const bool sp = a.softplus != 0;
+  const bool rev = (a.flags & kFlagReverse) != 0;
+  const bool tok = (a.flags & kFlagDeltaPerToken) != 0;
+  auto mrow = [&](int64_t t) { return rev ? L - 1 - t : t; };  // memory row of scan step t
 
-  __shared__ __attribute__((aligned(16))) float2 P[T][CPW];  // (dt, dt*u)
+  __shared__ __attribute__((aligned(16))) float2 P[T][CPW];  // (dt, dt*u), or (dt, u) with ZOH
   __shared__ __attribute__((aligned(16))) float E[T][CPW];   // dy * silu(z)
   __shared__ __attribute__((aligned(16))) float U[T][CPW];   // u
   __shared__ __attribute__((aligned(16))) float SG[T][CPW];  // d dt / d raw delta
@@ -180,12 +195,13 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
   const int64_t dc = dv ? d : D - 1;
   const float Dv = (MODE == 0 && a.Dskip) ? a.Dskip[dc] : 0.0f;
   int nst[NPL];
-  float Ap[NPL], An[NPL], lam[NPL], dAacc[NPL];
+  float Ap[NPL], An[NPL], Ainv[NPL], lam[NPL], dAacc[NPL];
 #pragma unroll
   for (int s = 0; s < NPL; ++s) {
     nst[s] = w * NPL + (s ^ par);
     An[s] = a.A[dc * N + nst[s]];
     Ap[s] = An[s] * kLog2e;
+    Ainv[s] = ZOH ? 1.0f / An[s] : 0.0f;
     dAacc[s] = 0.0f;
     float l0 = 0.0f;
     if (MODE == 0) {
@@ -206,8 +222,9 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int64_t t = t0 + tl0 + j * (NT / G);
-      const int64_t idx = (row0 + (t < te ? t : te - 1)) * D + dgc;
-      r_dl[j] = V::load(dl, idx);
+      const int64_t r = row0 + mrow(t < te ? t : te - 1);
+      const int64_t idx = r * D + dgc;
+      r_dl[j] = tok ? V::splat(dl, r) : V::load(dl, idx);
       r_dy[j] = V::load(dyp, idx);
       if (MODE == 0) r_u[j] = V::load(u, idx);
       if (has_z) r_z[j] = V::load(zz, idx);
@@ -217,7 +234,7 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
       const int i = tid + j * NT;
       if (BCN % NT == 0 || i < BCN) {
         const int64_t t = t0 + i / N;
-        const int64_t idx = (row0 + (t < te ? t : te - 1)) * N + i % N;
+        const int64_t idx = (row0 + mrow(t < te ? t : te - 1)) * N + i % N;
         if (MODE == 0) r_b[j] = load_io(Bm, idx);
         r_c[j] = load_io(Cm, idx);
       }
@@ -256,8 +273,13 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
         gz[q] = gzv;
       }
       float4 *pp = (float4 *)&P[tl][4 * g];
-      pp[0] = make_float4(dt[0], dt[0] * xv[0], dt[1], dt[1] * xv[1]);
-      pp[1] = make_float4(dt[2], dt[2] * xv[2], dt[3], dt[3] * xv[3]);
+      if (ZOH) {
+        pp[0] = make_float4(dt[0], xv[0], dt[1], xv[1]);
+        pp[1] = make_float4(dt[2], xv[2], dt[3], xv[3]);
+      } else {
+        pp[0] = make_float4(dt[0], dt[0] * xv[0], dt[1], dt[1] * xv[1]);
+        pp[1] = make_float4(dt[2], dt[2] * xv[2], dt[3], dt[3] * xv[3]);
+      }
       *(float4 *)&E[tl][4 * g] = make_float4(e[0], e[1], e[2], e[3]);
       if (MODE == 0) {
         *(float4 *)&U[tl][4 * g] = x4;
@@ -319,6 +341,7 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
       const int tq = (tid + j * NT) / CPW;  // channel of every item is the lane
       const int tl = tg * TE + tq;
       const int64_t t = t0 + tl;
+      float ddl = 0.0f;
       if (t < te && dv) {
         float pre = 0.0f, dua = 0.0f, dda = 0.0f;
 #pragma unroll
@@ -328,13 +351,18 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
           dda += Q[2][tq][ww][lane];
         }
         const float x = U[tl][lane], e = E[tl][lane], dt = P[tl][lane].x;
-        const float ddl = fmaf(x, dua, dda) * SG[tl][lane];
-        const int64_t idx = (row0 + t) * D + d;
-        store_io((IO *)a.du, idx, fmaf(Dv, e, dt * dua));
-        store_io((IO *)a.ddelta, idx, ddl);
+        // with ZOH the sweep already folded the input-coefficient terms in
+        ddl = (ZOH ? dda : fmaf(x, dua, dda)) * SG[tl][lane];
+        const int64_t idx = (row0 + mrow(t)) * D + d;
+        store_io((IO *)a.du, idx, fmaf(Dv, e, ZOH ? dua : dt * dua));
+        if (!tok) store_io((IO *)a.ddelta, idx, ddl);
         if (has_z) store_io((IO *)a.dz, idx, GZ[tl][lane] * fmaf(Dv, x, pre));
         dD_acc = fmaf(e, x, dD_acc);
         dbias_acc += ddl;
+      }
+      if (tok) {  // one step size per token: sum this wave's 64 channels
+        const float sdl = wave_sum(ddl);
+        if (lane == 0 && t < te) ws.partTok[(b * ws.ntiles + tile) * L + mrow(t)] = sdl;
       }
     }
   };
@@ -354,7 +382,7 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
     if (half == 0 && t < te && (NPL == 2 || (q & 1) == 0)) {
       const int n = NPL == 2 ? w * 2 + (q & 1) : w;
       float *dst = q < 2 ? ws.partB : ws.partC;
-      dst[((b * ws.ntiles + tile) * L + t) * N + n] = s;
+      dst[((b * ws.ntiles + tile) * L + mrow(t)) * N + n] = s;
     }
   };
 
@@ -381,7 +409,8 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
 #pragma unroll
         for (int s = 0; s < NPL; ++s) {
           const float da = fast_exp2(p.x * Ap[s]);
-          h[s] = fmaf(da, h[s], p.y * bv[s]);
+          const float cf = ZOH ? zoh_coef(p.x, p.x * An[s], da, Ainv[s]) : 1.0f;
+          h[s] = fmaf(da, h[s], ZOH ? cf * p.y * bv[s] : p.y * bv[s]);
           Hh[tl][s] = h[s];
           Ha[tl][s] = da;
         }
@@ -404,14 +433,26 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
           const float ht = Hh[tl][s];
           const float hp = tl > 0 ? Hh[tl > 0 ? tl - 1 : 0][s] : hs[s];
           const float lt = fmaf(e, cv[s], lam[s]);
+          const float da = Ha[tl][s];
           pre = fmaf(cv[s], ht, pre);
           cC[s] = e * ht;
-          cB[s] = lt * p.y;
-          dup = fmaf(lt, bv[s], dup);
-          lam[s] = Ha[tl][s] * lt;
+          lam[s] = da * lt;
           const float r = lam[s] * hp;
           ddp = fmaf(r, An[s], ddp);
           dAacc[s] = fmaf(r, p.x, dAacc[s]);
+          if (ZOH) {  // p.y is u; the coefficient and its derivatives enter every term
+            const float x = p.x * An[s];
+            const float cf = zoh_coef(p.x, x, da, Ainv[s]);
+            const float lu = lt * p.y;
+            cB[s] = lu * cf;
+            dup = fmaf(lt * cf, bv[s], dup);
+            const float q = lu * bv[s];
+            ddp = fmaf(q, da, ddp);
+            dAacc[s] = fmaf(q, zoh_dcoef_dA(p.x, x, da, cf, Ainv[s]), dAacc[s]);
+          } else {  // p.y is dt*u
+            cB[s] = lt * p.y;
+            dup = fmaf(lt, bv[s], dup);
+          }
         }
         Q[0][tq][w][lane] = pre;
         Q[1][tq][w][lane] = dup;
@@ -488,6 +529,18 @@ __global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(BwdArgs a, BwdWs ws)
   }
 }
 
+// Per-token ddelta: sum of the per-tile partials in tile order.
+template <typename IO>
+__global__ void __launch_bounds__(256) bwd_reduce_tok_kernel(BwdArgs a, BwdWs ws) {
+  const int64_t total = a.B * a.L;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t b = i / a.L, r = i % a.L;
+    float sd = 0.0f;
+    for (int64_t tile = 0; tile < ws.ntiles; ++tile) sd += ws.partTok[(b * ws.ntiles + tile) * a.L + r];
+    store_io((IO *)a.ddelta, i, sd);
+  }
+}
+
 // dA, dD, d bias: sum of the partials over batch rows and segments.
 __global__ void __launch_bounds__(256) bwd_reduce_params_kernel(BwdArgs a, BwdWs ws) {
   const int64_t DN = a.D * a.N;
@@ -516,15 +569,26 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
   const unsigned tiles = (unsigned)ws.ntiles;
   hipError_t e;
   if (ws.seg_len) {
-    hipLaunchKernelGGL((bwd_kernel<IO, N, 1>), dim3(tiles, (unsigned)a.B, (unsigned)(ws.nseg - 1)), dim3(NT), 0, s,
+    hipLaunchKernelGGL((bwd_kernel<IO, N, 1, false>), dim3(tiles, (unsigned)a.B, (unsigned)(ws.nseg - 1)), dim3(NT), 0, s,
                        a, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nst = a.B * a.D * a.N;
     hipLaunchKernelGGL(bwd_seg_combine_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, a, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((bwd_kernel<IO, N, 0>), dim3(tiles, (unsigned)a.B, (unsigned)ws.nseg), dim3(NT), 0, s, a, ws);
+  if (a.flags & kFlagZoh)
+    hipLaunchKernelGGL((bwd_kernel<IO, N, 0, true>), dim3(tiles, (unsigned)a.B, (unsigned)ws.nseg), dim3(NT), 0, s, a,
+                       ws);
+  else
+    hipLaunchKernelGGL((bwd_kernel<IO, N, 0, false>), dim3(tiles, (unsigned)a.B, (unsigned)ws.nseg), dim3(NT), 0, s, a,
+                       ws);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.flags & kFlagDeltaPerToken) {
+    int64_t tb = (a.B * a.L + 255) / 256;
+    if (tb > 65536) tb = 65536;
+    hipLaunchKernelGGL((bwd_reduce_tok_kernel<IO>), dim3((unsigned)tb), dim3(256), 0, s, a, ws);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int64_t total = a.B * a.L * a.N;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;

@@ -32,7 +32,11 @@ namespace ssm {
 // MODE 0: full forward (y, chunk states, final state).  MODE 1: first phase of
 // a sequence split: the segment's end state from a zero start, and the sum of
 // its step sizes (no y).  blockIdx.z is the segment.
-template <typename IO, int N, int NPL, int CPW, int T, int PD, int MODE>
+// ZOH: exact zero-order-hold input term expm1(dt A)/A * B * u (reading guide,
+// "Yöntem", discretisation of B) instead of dt * B * u.  The other options
+// (reverse direction, one step size per token, accumulate into y) are
+// runtime flags: steps are numbered in scan order and mapped to memory rows.
+template <typename IO, int N, int NPL, int CPW, int T, int PD, int MODE, bool ZOH>
 __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs a) {
   constexpr int NG = 64 / CPW;             // state groups per wave (lanes = CPW channels x NG groups)
   constexpr int NW = N / (NPL * NG);       // waves per workgroup
@@ -71,8 +75,12 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
   const int64_t K = (L + kChunkLen - 1) / kChunkLen;
   const bool has_z = MODE == 0 && a.z != nullptr;
   const bool sp = a.softplus != 0;
+  const bool rev = (a.flags & kFlagReverse) != 0;
+  const bool tok = (a.flags & kFlagDeltaPerToken) != 0;
+  const bool accum = (a.flags & kFlagAccumulate) != 0;
+  auto mrow = [&](int64_t t) { return rev ? L - 1 - t : t; };  // memory row of scan step t
 
-  __shared__ __attribute__((aligned(16))) float2 P[T][CPW];         // (dt, dt*u) per step and channel
+  __shared__ __attribute__((aligned(16))) float2 P[T][CPW];  // (dt, dt*u), or (dt, u) with ZOH
   __shared__ __attribute__((aligned(16))) float Y[T][NW][64];       // per-lane partial sum over its states
   __shared__ __attribute__((aligned(16))) float BC[T][NSP][2 * NPL];  // B then C values per state slice
 
@@ -99,12 +107,14 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
   const int64_t d = d0 + c;
   const bool dv = d < D;
   const int64_t dc = dv ? d : D - 1;
-  float Ap[NPL], h[NPL];
+  float Ap[NPL], An[NPL], Ainv[NPL], h[NPL];
   float dsum = 0.0f;  // MODE 1: sum of this channel's step sizes over the segment
 #pragma unroll
   for (int k = 0; k < NPL; ++k) {
     const int n = spi * NPL + k;
-    Ap[k] = a.A[dc * N + n] * kLog2e;
+    An[k] = a.A[dc * N + n];
+    Ap[k] = An[k] * kLog2e;
+    Ainv[k] = ZOH ? 1.0f / An[k] : 0.0f;
     if (MODE == 1)
       h[k] = 0.0f;
     else if (a.seg_len)
@@ -122,8 +132,9 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int64_t t = tb + k * T + tl0 + j * (NT / G);
-      const int64_t idx = (row0 + (t < te ? t : te - 1)) * D + dgc;
-      ra[j] = V::load(dl, idx);
+      const int64_t r = row0 + mrow(t < te ? t : te - 1);
+      const int64_t idx = r * D + dgc;
+      ra[j] = tok ? V::splat(dl, r) : V::load(dl, idx);
       ru[j] = V::load(u, idx);
       if (has_z) rz[j] = V::load(zz, idx);
     }
@@ -132,7 +143,7 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
       const int i = tid + j * NT;
       if (BCN % NT == 0 || i < BCN) {
         const int64_t t = tb + k * T + i / N;
-        const int64_t idx = (row0 + (t < te ? t : te - 1)) * N + i % N;
+        const int64_t idx = (row0 + mrow(t < te ? t : te - 1)) * N + i % N;
         rb[j] = load_io(Bm, idx);
         if (MODE == 0) rc[j] = load_io(Cm, idx);
       }
@@ -150,8 +161,13 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
 #pragma unroll
       for (int q = 0; q < 4; ++q) dt[q] = tv ? step_size(rv[q], bias4[q], sp) : 0.0f;
       float4 *pp = (float4 *)&P[tl][4 * g];
-      pp[0] = make_float4(dt[0], dt[0] * xv[0], dt[1], dt[1] * xv[1]);
-      pp[1] = make_float4(dt[2], dt[2] * xv[2], dt[3], dt[3] * xv[3]);
+      if (ZOH) {  // the input coefficient depends on the state: keep u itself
+        pp[0] = make_float4(dt[0], xv[0], dt[1], xv[1]);
+        pp[1] = make_float4(dt[2], xv[2], dt[3], xv[3]);
+      } else {
+        pp[0] = make_float4(dt[0], dt[0] * xv[0], dt[1], dt[1] * xv[1]);
+        pp[1] = make_float4(dt[2], dt[2] * xv[2], dt[3], dt[3] * xv[3]);
+      }
       keep_u[j] = x;
       if (has_z) {
         const float4 zv = V::cvt(rz[j]);
@@ -176,6 +192,7 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
       const int tl = tl0 + j * (NT / G);
       const int64_t t = tb + k * T + tl;
       if (t < te && gv) {
+        const int64_t yi = (row0 + mrow(t)) * D + dg;
         float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
@@ -189,7 +206,11 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
         s.y = fmaf(Dsk4[1], keep_u[j].y, s.y) * keep_g[j].y;
         s.z = fmaf(Dsk4[2], keep_u[j].z, s.z) * keep_g[j].z;
         s.w = fmaf(Dsk4[3], keep_u[j].w, s.w) * keep_g[j].w;
-        V::store(y, (row0 + t) * D + dg, s);
+        if (accum) {
+          const float4 o = V::cvt(V::load(y, yi));
+          s.x += o.x, s.y += o.y, s.z += o.z, s.w += o.w;
+        }
+        V::store(y, yi, s);
       }
     }
   };
@@ -232,7 +253,12 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
 #pragma unroll
         for (int kk = 0; kk < NPL; ++kk) {
           const float da = fast_exp2(p.x * Ap[kk]);
-          h[kk] = fmaf(da, h[kk], p.y * bc[kk]);
+          if (ZOH) {
+            const float cf = zoh_coef(p.x, p.x * An[kk], da, Ainv[kk]);
+            h[kk] = fmaf(da, h[kk], cf * p.y * bc[kk]);
+          } else {
+            h[kk] = fmaf(da, h[kk], p.y * bc[kk]);
+          }
           if (MODE == 0) ys = fmaf(bc[NPL + kk], h[kk], ys);
         }
         if (MODE == 0)
@@ -344,7 +370,7 @@ static int pick_cpw(const FwdArgs &a) {
   return wg64 <= device_cus() ? 64 : 32;
 }
 
-template <typename IO, int N, int CPW>
+template <typename IO, int N, int CPW, bool ZOH>
 static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   constexpr int NPL = N >= 2 ? 2 : 1;
   constexpr int NW = N * CPW / (64 * NPL);
@@ -355,7 +381,8 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   a.seg_len = split_len(a.B, a.L, a.D);
   const unsigned tiles = (unsigned)((a.D + CPW - 1) / CPW);
   if (a.seg_len == 0) {
-    hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0>), dim3(tiles, (unsigned)a.B, 1), dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0, ZOH>), dim3(tiles, (unsigned)a.B, 1), dim3(64 * NW), 0, s,
+                       a);
     return hipGetLastError();
   }
   const int64_t nseg = (a.L + a.seg_len - 1) / a.seg_len;
@@ -363,7 +390,7 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   a.seg_hloc = ws;
   a.seg_state = ws + a.B * nseg * a.D * a.N;
   a.seg_dsum = ws + 2 * a.B * nseg * a.D * a.N;
-  hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 1>), dim3(tiles, (unsigned)a.B, (unsigned)(nseg - 1)),
+  hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 1, ZOH>), dim3(tiles, (unsigned)a.B, (unsigned)(nseg - 1)),
                      dim3(64 * NW), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -371,7 +398,7 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   hipLaunchKernelGGL(fwd_seg_combine_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, a, nseg);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0>), dim3(tiles, (unsigned)a.B, (unsigned)nseg),
+  hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0, ZOH>), dim3(tiles, (unsigned)a.B, (unsigned)nseg),
                      dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
@@ -380,14 +407,16 @@ template <typename IO, int N>
 static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
   constexpr int NPL = N >= 2 ? 2 : 1;
   constexpr int mincpw = 64 * NPL / N > 16 ? 64 * NPL / N : 16;
+  if (a.flags & kFlagZoh)  // one tile width for the exact-hold variant (fewer instantiations)
+    return launch_fwd_cpw<IO, N, (mincpw > 32 ? 64 : 32), true>(a, s);
   const int cpw = pick_cpw<N>(a);
   if constexpr (mincpw <= 16) {
-    if (cpw == 16) return launch_fwd_cpw<IO, N, 16>(a, s);
+    if (cpw == 16) return launch_fwd_cpw<IO, N, 16, false>(a, s);
   }
   if constexpr (mincpw <= 32) {
-    if (cpw == 32) return launch_fwd_cpw<IO, N, 32>(a, s);
+    if (cpw == 32) return launch_fwd_cpw<IO, N, 32, false>(a, s);
   }
-  return launch_fwd_cpw<IO, N, 64>(a, s);
+  return launch_fwd_cpw<IO, N, 64, false>(a, s);
 }
 
 template <typename IO>

@@ -109,15 +109,17 @@ int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim,
   return ssm::bwd_workspace_bytes(batch, seqlen, dim, dstate, io_dtype);
 }
 
-int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
-                 const void *u, const void *delta, const float *A, const void *Bmat,
-                 const void *Cmat, const float *Dskip, const void *z, const float *delta_bias,
-                 int delta_softplus, const float *h0, float *h_final, void *y,
-                 float *chunk_states, void *workspace, int64_t workspace_bytes,
-                 void *hip_stream) {
+int ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                    const void *u, const void *delta, const float *A, const void *Bmat,
+                    const void *Cmat, const float *Dskip, const void *z, const float *delta_bias,
+                    int delta_softplus, const float *h0, float *h_final, void *y,
+                    float *chunk_states, void *workspace, int64_t workspace_bytes,
+                    void *hip_stream, int flags) {
   g_last_error[0] = 0;
   int st = check_sizes(batch, seqlen, dim, dstate, io_dtype);
   if (st != SSM_OK) return st;
+  if (flags & ~(SSM_FLAG_ZOH | SSM_FLAG_REVERSE | SSM_FLAG_DELTA_PER_TOKEN | SSM_FLAG_ACCUMULATE))
+    return fail(SSM_ERR_UNSUPPORTED, "unknown flags 0x%x for the forward scan", flags);
   const Ptr ps[] = {{"u", u, true},          {"delta", delta, true},   {"A", A, true},
                     {"Bmat", Bmat, true},    {"Cmat", Cmat, true},     {"y", y, true},
                     {"Dskip", Dskip, false}, {"z", z, false},          {"delta_bias", delta_bias, false},
@@ -129,22 +131,39 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(SSM_ERR_WORKSPACE, "forward needs %lld workspace bytes, got %lld", (long long)need,
                 (long long)(workspace ? workspace_bytes : 0));
-  ssm::FwdArgs a{batch, seqlen, dim, dstate, u,       delta, Bmat,         Cmat,
-                 z,     A,      Dskip, delta_bias, h0, delta_softplus != 0, h_final, y,
-                 chunk_states, workspace, workspace_bytes, 0, nullptr, nullptr, nullptr};
+  ssm::FwdArgs a{};
+  a.B = batch, a.L = seqlen, a.D = dim, a.N = dstate;
+  a.u = u, a.delta = delta, a.Bm = Bmat, a.Cm = Cmat, a.z = z;
+  a.A = A, a.Dskip = Dskip, a.bias = delta_bias, a.h0 = h0;
+  a.softplus = delta_softplus != 0, a.flags = flags;
+  a.h_final = h_final, a.y = y, a.chunk_states = chunk_states;
+  a.workspace = workspace, a.workspace_bytes = workspace_bytes;
   return hip_status(ssm::launch_fwd(a, io_dtype, (hipStream_t)hip_stream), "ssm_scan_fwd launch");
 }
 
-int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
                  const void *u, const void *delta, const float *A, const void *Bmat,
                  const void *Cmat, const float *Dskip, const void *z, const float *delta_bias,
-                 int delta_softplus, const float *h0, const float *chunk_states, const void *dy,
-                 const float *dh_final, void *du, void *ddelta, float *dA, void *dB, void *dC,
-                 float *dD, void *dz, float *ddelta_bias, float *dh0, void *workspace,
-                 int64_t workspace_bytes, void *hip_stream) {
+                 int delta_softplus, const float *h0, float *h_final, void *y,
+                 float *chunk_states, void *workspace, int64_t workspace_bytes,
+                 void *hip_stream) {
+  return ssm_scan_fwd_ex(batch, seqlen, dim, dstate, io_dtype, u, delta, A, Bmat, Cmat, Dskip, z,
+                         delta_bias, delta_softplus, h0, h_final, y, chunk_states, workspace,
+                         workspace_bytes, hip_stream, 0);
+}
+
+int ssm_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                    const void *u, const void *delta, const float *A, const void *Bmat,
+                    const void *Cmat, const float *Dskip, const void *z, const float *delta_bias,
+                    int delta_softplus, const float *h0, const float *chunk_states, const void *dy,
+                    const float *dh_final, void *du, void *ddelta, float *dA, void *dB, void *dC,
+                    float *dD, void *dz, float *ddelta_bias, float *dh0, void *workspace,
+                    int64_t workspace_bytes, void *hip_stream, int flags) {
   g_last_error[0] = 0;
   int st = check_sizes(batch, seqlen, dim, dstate, io_dtype);
   if (st != SSM_OK) return st;
+  if (flags & ~(SSM_FLAG_ZOH | SSM_FLAG_REVERSE | SSM_FLAG_DELTA_PER_TOKEN))
+    return fail(SSM_ERR_UNSUPPORTED, "unknown or forward-only flags 0x%x for the backward scan", flags);
   const Ptr ps[] = {{"u", u, true},
                     {"delta", delta, true},
                     {"A", A, true},
@@ -177,19 +196,39 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int
   if (workspace_bytes < need)
     return fail(SSM_ERR_WORKSPACE, "backward needs %lld workspace bytes, got %lld", (long long)need,
                 (long long)workspace_bytes);
-  ssm::BwdArgs a{batch, seqlen, dim, dstate, u,  delta, Bmat, Cmat, z,  dy,     A,  Dskip,
-                 delta_bias, h0, chunk_states, dh_final, delta_softplus != 0, du, ddelta, dB, dC,
-                 dz, dA, dD, ddelta_bias, dh0, workspace, workspace_bytes};
+  ssm::BwdArgs a{};
+  a.B = batch, a.L = seqlen, a.D = dim, a.N = dstate;
+  a.u = u, a.delta = delta, a.Bm = Bmat, a.Cm = Cmat, a.z = z, a.dy = dy;
+  a.A = A, a.Dskip = Dskip, a.bias = delta_bias, a.h0 = h0, a.chunk_states = chunk_states;
+  a.dh_final = dh_final, a.softplus = delta_softplus != 0, a.flags = flags;
+  a.du = du, a.ddelta = ddelta, a.dB = dB, a.dC = dC, a.dz = dz;
+  a.dA = dA, a.dD = dD, a.dbias = ddelta_bias, a.dh0 = dh0;
+  a.workspace = workspace, a.workspace_bytes = workspace_bytes;
   return hip_status(ssm::launch_bwd(a, io_dtype, (hipStream_t)hip_stream), "ssm_scan_bwd launch");
 }
 
-int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, float *state,
-                     const void *u, const void *delta, const float *A, const void *Bmat,
-                     const void *Cmat, const float *Dskip, const void *z,
-                     const float *delta_bias, int delta_softplus, void *y, void *hip_stream) {
+int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                 const void *u, const void *delta, const float *A, const void *Bmat,
+                 const void *Cmat, const float *Dskip, const void *z, const float *delta_bias,
+                 int delta_softplus, const float *h0, const float *chunk_states, const void *dy,
+                 const float *dh_final, void *du, void *ddelta, float *dA, void *dB, void *dC,
+                 float *dD, void *dz, float *ddelta_bias, float *dh0, void *workspace,
+                 int64_t workspace_bytes, void *hip_stream) {
+  return ssm_scan_bwd_ex(batch, seqlen, dim, dstate, io_dtype, u, delta, A, Bmat, Cmat, Dskip, z,
+                         delta_bias, delta_softplus, h0, chunk_states, dy, dh_final, du, ddelta, dA,
+                         dB, dC, dD, dz, ddelta_bias, dh0, workspace, workspace_bytes, hip_stream, 0);
+}
+
+int ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, float *state,
+                        const void *u, const void *delta, const float *A, const void *Bmat,
+                        const void *Cmat, const float *Dskip, const void *z,
+                        const float *delta_bias, int delta_softplus, void *y, void *hip_stream,
+                        int flags) {
   g_last_error[0] = 0;
   int st = check_sizes(batch, 1, dim, dstate, io_dtype);
   if (st != SSM_OK) return st;
+  if (flags & ~SSM_FLAG_ZOH)
+    return fail(SSM_ERR_UNSUPPORTED, "only SSM_FLAG_ZOH applies to a single-token update (got 0x%x)", flags);
   // state and A are accessed 16 bytes at a time; the per-token tensors only
   // need the natural alignment of their element type.
   const Ptr ps[] = {{"state", state, true}, {"A", A, true}};
@@ -205,9 +244,20 @@ int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, f
     if (((uintptr_t)q.p % need) != 0)
       return fail(SSM_ERR_ALIGNMENT, "%s is not aligned to its element size", q.name);
   }
-  ssm::DecodeArgs a{batch, dim, dstate, state, u, delta, Bmat, Cmat, z, A, Dskip, delta_bias,
-                    delta_softplus != 0, y};
+  ssm::DecodeArgs a{};
+  a.B = batch, a.D = dim, a.N = dstate, a.state = state;
+  a.u = u, a.delta = delta, a.Bm = Bmat, a.Cm = Cmat, a.z = z;
+  a.A = A, a.Dskip = Dskip, a.bias = delta_bias, a.softplus = delta_softplus != 0, a.flags = flags;
+  a.y = y;
   return hip_status(ssm::launch_decode(a, io_dtype, (hipStream_t)hip_stream), "ssm_state_update launch");
+}
+
+int ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, float *state,
+                     const void *u, const void *delta, const float *A, const void *Bmat,
+                     const void *Cmat, const float *Dskip, const void *z,
+                     const float *delta_bias, int delta_softplus, void *y, void *hip_stream) {
+  return ssm_state_update_ex(batch, dim, dstate, io_dtype, state, u, delta, A, Bmat, Cmat, Dskip, z,
+                             delta_bias, delta_softplus, y, hip_stream, 0);
 }
 
 }  // extern "C"

@@ -14,7 +14,9 @@
 
 namespace ssm {
 
-template <typename IO, int N>
+// ZOH: exact zero-order-hold input term expm1(dt A)/A * B * u (reading
+// guide, "Yöntem", discretisation of B) instead of dt * B * u.
+template <typename IO, int N, bool ZOH>
 __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   constexpr int SPL = N < 4 ? N : 4;
   constexpr int LPC = N / SPL;
@@ -45,7 +47,13 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < SPL; ++k) {
     const int64_t bn = b * N + g * SPL + k;
-    st[k] = fmaf(fast_exp2(dt * Av[k] * kLog2e), st[k], dtu * load_io(Bm, bn));
+    const float da = fast_exp2(dt * Av[k] * kLog2e);
+    if (ZOH) {
+      const float cf = zoh_coef(dt, dt * Av[k], da, 1.0f / Av[k]);
+      st[k] = fmaf(da, st[k], cf * x * load_io(Bm, bn));
+    } else {
+      st[k] = fmaf(da, st[k], dtu * load_io(Bm, bn));
+    }
     ys = fmaf(load_io(Cm, bn), st[k], ys);
   }
 #pragma unroll
@@ -68,7 +76,11 @@ template <typename IO, int N>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
   constexpr int LPC = N < 4 ? 1 : N / 4;
   const int64_t threads = a.B * a.D * LPC;
-  hipLaunchKernelGGL((decode_kernel<IO, N>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (a.flags & kFlagZoh)
+    hipLaunchKernelGGL((decode_kernel<IO, N, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<IO, N, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

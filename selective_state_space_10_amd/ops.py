@@ -48,6 +48,15 @@ def chunk_len() -> int:
     return int(_lib.load().ssm_scan_chunk_len())
 
 
+def _flags(delta, u, zoh=False, reverse=False, accumulate=False):
+    f = (_lib.FLAG_ZOH if zoh else 0) | (_lib.FLAG_REVERSE if reverse else 0)
+    if accumulate:
+        f |= _lib.FLAG_ACCUMULATE
+    if isinstance(delta, torch.Tensor) and delta.dim() == 2:
+        f |= _lib.FLAG_DELTA_PER_TOKEN
+    return f
+
+
 def _check_common(u, delta, A, B, C, D, z, delta_bias, h0):
     if not isinstance(u, torch.Tensor) or u.dim() != 3:
         raise ValueError("u must be a (batch, seqlen, dim) tensor")
@@ -60,7 +69,10 @@ def _check_common(u, delta, A, B, C, D, z, delta_bias, h0):
         raise ValueError(f"tensors must be on a GPU device, got {dev}")
     _io_code(u)
     _need("u", u, (Bsz, L, Dm), io, dev)
-    _need("delta", delta, (Bsz, L, Dm), io, dev)
+    if isinstance(delta, torch.Tensor) and delta.dim() == 2:  # one step size per token
+        _need("delta", delta, (Bsz, L), io, dev)
+    else:
+        _need("delta", delta, (Bsz, L, Dm), io, dev)
     _need("A", A, (Dm, N), torch.float32, dev)
     _need("B", B, (Bsz, L, N), io, dev)
     _need("C", C, (Bsz, L, N), io, dev)
@@ -72,14 +84,24 @@ def _check_common(u, delta, A, B, C, D, z, delta_bias, h0):
 
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, h0=None,
-             return_final_state=False, save_chunk_states=False):
+             return_final_state=False, save_chunk_states=False, zoh=False, reverse=False,
+             out=None):
     """Forward selective scan.  Returns (y, h_final or None, chunk_states or None);
-    chunk_states is (batch, K, dstate, dim) with K = ceil(seqlen / chunk_len())."""
+    chunk_states is (batch, K, dstate, dim) with K = ceil(seqlen / chunk_len()).
+
+    Options: ``zoh`` uses the exact zero-order-hold input term; ``reverse``
+    scans from the last step to the first; a (batch, seqlen) ``delta`` is one
+    step size per token; ``out`` (a tensor like u) receives y += result."""
     Bsz, L, Dm, N = _check_common(u, delta, A, B, C, D, z, delta_bias, h0)
     lib = _lib.load()
     io = _io_code(u)
     dev = u.device
-    y = torch.empty_like(u)
+    if out is not None:
+        _need("out", out, (Bsz, L, Dm), u.dtype, dev)
+        y = out
+    else:
+        y = torch.empty_like(u)
+    flags = _flags(delta, u, zoh, reverse, accumulate=out is not None)
     hf = torch.empty((Bsz, Dm, N), dtype=torch.float32, device=dev) if return_final_state else None
     cs = None
     if save_chunk_states:
@@ -90,16 +112,18 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
         raise ValueError("invalid sizes for the forward workspace query")
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb > 0 else None
     with torch.cuda.device(dev):
-        st = lib.ssm_scan_fwd(Bsz, L, Dm, N, io, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                              _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)),
-                              _ptr(h0), _ptr(hf), _ptr(y), _ptr(cs), _ptr(ws), wsb, _stream(dev))
+        st = lib.ssm_scan_fwd_ex(Bsz, L, Dm, N, io, _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                                 _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                 int(bool(delta_softplus)), _ptr(h0), _ptr(hf), _ptr(y), _ptr(cs),
+                                 _ptr(ws), wsb, _stream(dev), flags)
     _lib.check(st)
     return y, hf, cs
 
 
 def scan_bwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, chunk_states, dy,
-             dh_final=None, want_ddelta_bias=True, want_dh0=True):
-    """Backward of scan_fwd.  Returns a dict: du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0."""
+             dh_final=None, want_ddelta_bias=True, want_dh0=True, zoh=False, reverse=False):
+    """Backward of scan_fwd (same options; ddelta has delta's shape).  Returns a
+    dict: du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0."""
     Bsz, L, Dm, N = _check_common(u, delta, A, B, C, D, z, delta_bias, h0)
     lib = _lib.load()
     io = _io_code(u)
@@ -109,7 +133,7 @@ def scan_bwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, chunk_stat
     _need("dy", dy, (Bsz, L, Dm), u.dtype, dev)
     _need("dh_final", dh_final, (Bsz, Dm, N), torch.float32, dev, optional=True)
     f32 = dict(dtype=torch.float32, device=dev)
-    g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(u), dA=torch.empty((Dm, N), **f32),
+    g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(delta), dA=torch.empty((Dm, N), **f32),
              dB=torch.empty_like(B), dC=torch.empty_like(C),
              dD=torch.empty((Dm,), **f32) if D is not None else None,
              dz=torch.empty_like(u) if z is not None else None,
@@ -119,18 +143,21 @@ def scan_bwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, chunk_stat
     wsb = int(lib.ssm_scan_bwd_workspace_bytes(Bsz, L, Dm, N, io))
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
-        st = lib.ssm_scan_bwd(Bsz, L, Dm, N, io, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                              _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)),
-                              _ptr(h0), _ptr(chunk_states), _ptr(dy), _ptr(dh_final),
-                              _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
-                              _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]),
-                              _ptr(g["dh0"]), _ptr(ws), wsb, _stream(dev))
+        st = lib.ssm_scan_bwd_ex(Bsz, L, Dm, N, io, _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                                 _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                 int(bool(delta_softplus)), _ptr(h0), _ptr(chunk_states), _ptr(dy),
+                                 _ptr(dh_final), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                                 _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
+                                 _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), _ptr(ws), wsb,
+                                 _stream(dev), _flags(delta, u, zoh, reverse))
     _lib.check(st)
     return g
 
 
-def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True):
-    """One decode step; ``state`` (batch, dim, dstate) fp32 is updated in place.  Returns y."""
+def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                 zoh=False):
+    """One decode step; ``state`` (batch, dim, dstate) fp32 is updated in place.  Returns y.
+    ``zoh`` uses the exact zero-order-hold input term."""
     if not isinstance(state, torch.Tensor) or state.dim() != 3:
         raise ValueError("state must be a (batch, dim, dstate) tensor")
     Bsz, Dm, N = state.shape
@@ -152,9 +179,10 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delt
     lib = _lib.load()
     y = torch.empty_like(u)
     with torch.cuda.device(dev):
-        st = lib.ssm_state_update(Bsz, Dm, N, io, _ptr(state), _ptr(u), _ptr(delta), _ptr(A),
-                                  _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-                                  int(bool(delta_softplus)), _ptr(y), _stream(dev))
+        st = lib.ssm_state_update_ex(Bsz, Dm, N, io, _ptr(state), _ptr(u), _ptr(delta), _ptr(A),
+                                     _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                     int(bool(delta_softplus)), _ptr(y), _stream(dev),
+                                     _lib.FLAG_ZOH if zoh else 0)
     _lib.check(st)
     return y
 
@@ -165,10 +193,12 @@ class SelectiveScanFn(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
-                h0=None):
+                h0=None, zoh=False, reverse=False):
         y, hf, cs = scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0,
-                             return_final_state=True, save_chunk_states=True)
+                             return_final_state=True, save_chunk_states=True, zoh=zoh,
+                             reverse=reverse)
         ctx.delta_softplus = bool(delta_softplus)
+        ctx.zoh, ctx.reverse = bool(zoh), bool(reverse)
         ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, h0, cs)
         return y, hf
 
@@ -177,12 +207,24 @@ class SelectiveScanFn(torch.autograd.Function):
         u, delta, A, B, C, D, z, delta_bias, h0, cs = ctx.saved_tensors
         g = scan_bwd(u, delta, A, B, C, D, z, delta_bias, ctx.delta_softplus, h0, cs,
                      dy.contiguous(), None if dhf is None else dhf.contiguous(),
-                     want_ddelta_bias=delta_bias is not None, want_dh0=h0 is not None)
+                     want_ddelta_bias=delta_bias is not None, want_dh0=h0 is not None,
+                     zoh=ctx.zoh, reverse=ctx.reverse)
         return (g["du"], g["ddelta"], g["dA"], g["dB"], g["dC"], g["dD"], g["dz"],
-                g["ddelta_bias"], None, g["dh0"])
+                g["ddelta_bias"], None, g["dh0"], None, None)
 
 
 def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
-                   h0=None):
+                   h0=None, zoh=False, reverse=False):
     """Differentiable scan; returns (y, h_final)."""
-    return SelectiveScanFn.apply(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0)
+    return SelectiveScanFn.apply(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, zoh,
+                                 reverse)
+
+
+def bidirectional_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                       zoh=False):
+    """Both scan directions summed: y = (S_fwd(u) + S_rev(u) + D u) * silu(z), where
+    S_fwd and S_rev are the state contributions sum_n C h of the forward and the
+    reverse recurrence.  Two launches; the second adds into the first's output."""
+    y, _, _ = scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, zoh=zoh)
+    scan_fwd(u, delta, A, B, C, None, z, delta_bias, delta_softplus, zoh=zoh, reverse=True, out=y)
+    return y

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_queries(lib):
-    assert lib.ssm_abi_version() == 1
+    assert lib.ssm_abi_version() == 2
     T = lib.ssm_scan_chunk_len()
     assert T >= 16 and T & (T - 1) == 0
     assert lib.ssm_scan_chunk_states_bytes(2, T * 3 + 1, 64, 16) == 2 * 4 * 64 * 16 * 4
@@ -119,6 +119,25 @@ def test_decode_validation(lib):
     assert f(2, 8, 4, 0, FAKE + 2, *args[1:], 1, FAKE, None) == ALIGNMENT  # state
     assert f(2, 8, 4, 0, *args[:3], FAKE + 8, *args[4:], 1, FAKE, None) == ALIGNMENT  # A
     assert f(2, 8, 4, 1, *args[:4], FAKE + 1, *args[5:], 1, FAKE, None) == ALIGNMENT  # odd bf16
+
+
+def test_option_flags_are_validated(lib):
+    """Unknown option bits, and bits that do not apply to an entry point, are
+    rejected before anything is enqueued."""
+    fargs = (1, 16, 8, 4, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, None, None, FAKE,
+             None, None, 0, None)
+    assert lib.ssm_scan_fwd_ex(*fargs, 16) == UNSUPPORTED
+    assert lib.ssm_scan_fwd_ex(*fargs, -1) == UNSUPPORTED
+    assert lib.ssm_scan_fwd_ex(*fargs[:1], 0, *fargs[2:], 1) == BAD_SHAPE  # sizes still checked
+    bargs = (1, 16, 8, 4, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, None, FAKE, FAKE,
+             None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, None, FAKE, 0, None)
+    assert lib.ssm_scan_bwd_ex(*bargs, 8) == UNSUPPORTED  # accumulate is forward-only
+    assert lib.ssm_scan_bwd_ex(*bargs, 32) == UNSUPPORTED
+    assert lib.ssm_scan_bwd_ex(*bargs, 7) == WORKSPACE  # valid bits: fails later, on the workspace
+    dargs = (2, 8, 4, 0) + (FAKE,) * 6 + (None, None, None, 1, FAKE, None)
+    assert lib.ssm_state_update_ex(*dargs, 2) == UNSUPPORTED  # no direction for one token
+    assert lib.ssm_state_update_ex(*dargs, 4) == UNSUPPORTED
+    assert b"SSM_FLAG_ZOH" in lib.ssm_last_error()
 
 
 def test_last_error_is_thread_local(lib):

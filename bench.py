@@ -11,9 +11,12 @@ line (rank 0).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-``--workload`` also accepts the other shapes (mamba-2.8b-layer-fwd,
-decode-state-update, million-length-fwd, million-length-bwd); their lines use
-the same keys and are for reference, the default workload is the headline.
+``--workload`` also accepts the other shapes and options (mamba-2.8b-layer-fwd,
+decode-state-update, million-length-fwd, million-length-bwd,
+mamba-370m-layer-bwd, the 370m forward with the exact zero-order hold, with one
+step size per token, or bidirectional, and the decode step with the exact
+hold); their lines use the same keys and are for reference, the default
+workload is the headline.
 """
 from __future__ import annotations
 
@@ -28,6 +31,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+WORKLOAD_NAMES = ["mamba-370m-layer-fwd", "mamba-2.8b-layer-fwd", "decode-state-update",
+                  "million-length-fwd", "million-length-bwd", "mamba-370m-layer-bwd",
+                  "mamba-370m-layer-fwd-zoh", "mamba-370m-layer-fwd-token-delta",
+                  "mamba-370m-layer-bidirectional", "decode-state-update-zoh"]
 METRIC = "selective-scan fwd tokens·channels/s and HBM GB/s (% of peak), Mamba-370m shape"
 UNIT = "tokens*channels/s"
 
@@ -37,9 +44,7 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mamba-370m-layer-fwd",
-                    choices=["mamba-370m-layer-fwd", "mamba-2.8b-layer-fwd", "decode-state-update",
-                             "million-length-fwd", "million-length-bwd"])
+    ap.add_argument("--workload", default="mamba-370m-layer-fwd", choices=WORKLOAD_NAMES)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=3, help="input sets rotated between steps")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -148,29 +153,41 @@ def copy_calibration(nbytes=1 << 30, reps=5):
             "bytes_written_per_launch": nbytes, "launches": reps}
 
 
-def bench_fwd(args, idx, name):
+def bench_fwd(args, idx, name, zoh=False, per_token=False, bidirectional=False):
+    """Forward scan of workload ``idx``; options: the exact zero-order-hold
+    input term, one step size per token (delta drawn as (B, L)), or both scan
+    directions summed (two launches, the second accumulating into y)."""
     import torch
 
     import selective_state_space_10_amd as m
     from workloads import WORKLOADS, algorithmic_bytes_fwd, workload_inputs
     w = WORKLOADS[idx]
-    want_hf = "h_final" in w.outputs
+    want_hf = "h_final" in w.outputs and not bidirectional
     sets = [workload_inputs(idx, device="cuda", seed=idx + 100 * r) for r in range(args.rotate)]
+    if per_token:  # one raw step size per token: the first channel's draw
+        sets = [dict(p, delta=p["delta"][:, :, 0].contiguous()) for p in sets]
     torch.cuda.synchronize()
 
     def step(p):
-        m.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["delta_bias"],
-                   True, None, return_final_state=want_hf)
+        if bidirectional:
+            m.bidirectional_scan(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                                 p["delta_bias"], True, zoh=zoh)
+        else:
+            m.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                       p["delta_bias"], True, None, return_final_state=want_hf, zoh=zoh)
 
     ms_step, ms_launch, wall = _time_launches(step, args.steps, args.warmup, sets)
     Bsz, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
     io_bytes = 4 if w.io_dtype == torch.float32 else 2
     nbytes = algorithmic_bytes_fwd(Bsz, L, D, N, io_bytes, h_final=want_hf)
+    if per_token:  # delta is (B, L) instead of (B, L, D)
+        nbytes -= Bsz * L * (D - 1) * io_bytes
     achieved = nbytes / (ms_launch * 1e-3) / 1e9
     sha = _source_sha("scan_fwd.hip", "device_common.hpp", "kernels.hpp")
     traffic = _traffic(f"fwd:{name}", sha)
     line = {
-        "metric": METRIC if idx == 1 else f"selective-scan fwd tokens*channels/s, {name}",
+        "metric": (METRIC if idx == 1 and name == "mamba-370m-layer-fwd"
+                   else f"selective-scan fwd tokens*channels/s, {name}"),
         "value": Bsz * L * D / (ms_step * 1e-3),
         "unit": UNIT, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -180,20 +197,26 @@ def bench_fwd(args, idx, name):
         "config": {"workload": name, "batch": Bsz, "seqlen": L, "dim": D, "dstate": N,
                    "io_dtype": str(w.io_dtype).replace("torch.", ""), "outputs": list(w.outputs),
                    "gpu": torch.cuda.get_device_name(), "wall_s": round(wall, 4),
-                   "prewarm_steps": _time_launches.prewarm_steps},
+                   "prewarm_steps": _time_launches.prewarm_steps,
+                   "options": {"zoh": zoh, "delta_per_token": per_token,
+                               "bidirectional": bidirectional}},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes": nbytes,
+                     "traffic": traffic if not (zoh or per_token or bidirectional) else None,
+                     "algorithmic_bytes": nbytes,
                      "kernel_ms": ms_launch, "source_sha": sha},
     }
-    if not args.no_cpu_baseline and idx == 1:
+    if bidirectional:
+        line["roofline"]["note"] = ("two launches per step; algorithmic bytes are one read of "
+                                    "the inputs and one write of y")
+    if not args.no_cpu_baseline and name == "mamba-370m-layer-fwd":
         pc = workload_inputs(idx, device="cuda", seed=idx)
         pc = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in pc.items()}
         line["cpu_baseline"] = _cpu_baseline_fwd(pc)
     return line
 
 
-def bench_decode(args):
+def bench_decode(args, zoh=False):
     import torch
 
     import selective_state_space_10_amd as m
@@ -206,7 +229,7 @@ def bench_decode(args):
     def step(t):
         st = states[t % len(states)]
         m.state_update(st, d["u"][t], d["delta"][t], d["A"], d["B"][t], d["C"][t], d["D"],
-                       d["z"][t], d["delta_bias"], True)
+                       d["z"][t], d["delta_bias"], True, zoh=zoh)
 
     ms_step, ms_launch, wall = _time_launches(step, args.steps, args.warmup, tok)
     nbytes = algorithmic_bytes_decode(w.batch, w.dim, w.dstate, 2)
@@ -215,24 +238,27 @@ def bench_decode(args):
             "value": w.batch * w.dim / (ms_step * 1e-3), "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16 storage, f32 compute",
-            "data": "synthetic", "config": {"workload": "decode-state-update", "batch": w.batch,
-                                            "dim": w.dim, "dstate": w.dstate,
-                                            "prewarm_steps": _time_launches.prewarm_steps},
+            "data": "synthetic", "config": {"workload": "decode-state-update" + ("-zoh" if zoh else ""),
+                                            "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
+                                            "prewarm_steps": _time_launches.prewarm_steps,
+                                            "options": {"zoh": zoh}},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                          "algorithmic_bytes": nbytes, "kernel_ms": ms_launch}}
 
 
-def bench_bwd(args):
+def bench_bwd(args, idx, name):
+    """Backward of workload ``idx`` (one forward with chunk states runs first,
+    outside the timed steps)."""
     import torch
 
     import selective_state_space_10_amd as m
     from workloads import WORKLOADS, cotangent, workload_inputs
-    w = WORKLOADS[4]
-    p = workload_inputs(4, device="cuda")
+    w = WORKLOADS[idx]
+    p = workload_inputs(idx, device="cuda")
     y, _, cs = m.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
                           p["delta_bias"], True, None, save_chunk_states=True)
-    dy = cotangent(y, 4)
+    dy = cotangent(y, idx)
     del y
 
     def step(_):
@@ -241,14 +267,18 @@ def bench_bwd(args):
 
     ms_step, ms_launch, wall = _time_launches(step, args.steps, args.warmup, [0])
     Bsz, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
-    nbytes = (4 * Bsz * L * D * 2 + 3 * Bsz * L * D * 2 + 4 * Bsz * L * N * 2 + cs.numel() * 4
+    io = 4 if w.io_dtype == torch.float32 else 2
+    # u, delta, z, dy in; du, ddelta, dz out; B, C in and dB, dC out; chunk states in; A, D,
+    # bias in and dA, dD, dbias out
+    nbytes = (7 * Bsz * L * D * io + 4 * Bsz * L * N * io + cs.numel() * 4
               + D * N * 4 * 2 + D * 4 * 4)
     achieved = nbytes / (ms_launch * 1e-3) / 1e9
-    return {"metric": "selective-scan bwd tokens*channels/s, million-length", "unit": UNIT,
+    return {"metric": f"selective-scan bwd tokens*channels/s, {name}", "unit": UNIT,
             "value": Bsz * L * D / (ms_step * 1e-3), "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "bf16 storage, f32 compute",
-            "data": "synthetic", "config": {"workload": "million-length-bwd", "batch": Bsz,
+            "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32" if io == 4 else "bf16 storage, f32 compute",
+            "data": "synthetic", "config": {"workload": name, "batch": Bsz,
                                             "seqlen": L, "dim": D, "dstate": N,
                                             "prewarm_steps": _time_launches.prewarm_steps},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
@@ -271,17 +301,28 @@ def main():
         return
     import selective_state_space_10_amd as m
     m.load()
-    if args.workload == "mamba-370m-layer-fwd":
-        line = bench_fwd(args, 1, args.workload)
-    elif args.workload == "mamba-2.8b-layer-fwd":
-        line = bench_fwd(args, 2, args.workload)
-    elif args.workload == "million-length-fwd":
+    wl = args.workload
+    if wl == "mamba-370m-layer-fwd":
+        line = bench_fwd(args, 1, wl)
+    elif wl == "mamba-370m-layer-fwd-zoh":
+        line = bench_fwd(args, 1, wl, zoh=True)
+    elif wl == "mamba-370m-layer-fwd-token-delta":
+        line = bench_fwd(args, 1, wl, per_token=True)
+    elif wl == "mamba-370m-layer-bidirectional":
+        line = bench_fwd(args, 1, wl, bidirectional=True)
+    elif wl == "mamba-2.8b-layer-fwd":
+        line = bench_fwd(args, 2, wl)
+    elif wl == "million-length-fwd":
         args.rotate = 1
-        line = bench_fwd(args, 4, args.workload)
-    elif args.workload == "decode-state-update":
+        line = bench_fwd(args, 4, wl)
+    elif wl == "decode-state-update":
         line = bench_decode(args)
+    elif wl == "decode-state-update-zoh":
+        line = bench_decode(args, zoh=True)
+    elif wl == "mamba-370m-layer-bwd":
+        line = bench_bwd(args, 1, wl)
     else:
-        line = bench_bwd(args)
+        line = bench_bwd(args, 4, wl)
     print(json.dumps(line), flush=True)
 
 

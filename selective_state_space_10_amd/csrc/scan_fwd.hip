@@ -33,10 +33,11 @@ namespace ssm {
 // a sequence split: the segment's end state from a zero start, and the sum of
 // its step sizes (no y).  blockIdx.z is the segment.
 // ZOH: exact zero-order-hold input term expm1(dt A)/A * B * u (reading guide,
-// "Yöntem", discretisation of B) instead of dt * B * u.  The other options
-// (reverse direction, one step size per token, accumulate into y) are
-// runtime flags: steps are numbered in scan order and mapped to memory rows.
-template <typename IO, int N, int NPL, int CPW, int T, int PD, int MODE, bool ZOH>
+// "Yöntem", discretisation of B) instead of dt * B * u.  FLAGS: the other
+// options (reverse direction, one step size per token, accumulate into y) are
+// honoured as runtime flags, with steps numbered in scan order and mapped to
+// memory rows; the plain variant (FLAGS false) carries none of that code.
+template <typename IO, int N, int NPL, int CPW, int T, int PD, int MODE, bool ZOH, bool FLAGS>
 __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs a) {
   constexpr int NG = 64 / CPW;             // state groups per wave (lanes = CPW channels x NG groups)
   constexpr int NW = N / (NPL * NG);       // waves per workgroup
@@ -75,9 +76,9 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
   const int64_t K = (L + kChunkLen - 1) / kChunkLen;
   const bool has_z = MODE == 0 && a.z != nullptr;
   const bool sp = a.softplus != 0;
-  const bool rev = (a.flags & kFlagReverse) != 0;
-  const bool tok = (a.flags & kFlagDeltaPerToken) != 0;
-  const bool accum = (a.flags & kFlagAccumulate) != 0;
+  const bool rev = FLAGS && (a.flags & kFlagReverse) != 0;
+  const bool tok = FLAGS && (a.flags & kFlagDeltaPerToken) != 0;
+  const bool accum = FLAGS && (a.flags & kFlagAccumulate) != 0;
   auto mrow = [&](int64_t t) { return rev ? L - 1 - t : t; };  // memory row of scan step t
 
   __shared__ __attribute__((aligned(16))) float2 P[T][CPW];  // (dt, dt*u), or (dt, u) with ZOH
@@ -370,7 +371,7 @@ static int pick_cpw(const FwdArgs &a) {
   return wg64 <= device_cus() ? 64 : 32;
 }
 
-template <typename IO, int N, int CPW, bool ZOH>
+template <typename IO, int N, int CPW, bool ZOH, bool FLAGS>
 static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   constexpr int NPL = N >= 2 ? 2 : 1;
   constexpr int NW = N * CPW / (64 * NPL);
@@ -381,7 +382,7 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   a.seg_len = split_len(a.B, a.L, a.D);
   const unsigned tiles = (unsigned)((a.D + CPW - 1) / CPW);
   if (a.seg_len == 0) {
-    hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0, ZOH>), dim3(tiles, (unsigned)a.B, 1), dim3(64 * NW), 0, s,
+    hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0, ZOH, FLAGS>), dim3(tiles, (unsigned)a.B, 1), dim3(64 * NW), 0, s,
                        a);
     return hipGetLastError();
   }
@@ -390,7 +391,7 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   a.seg_hloc = ws;
   a.seg_state = ws + a.B * nseg * a.D * a.N;
   a.seg_dsum = ws + 2 * a.B * nseg * a.D * a.N;
-  hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 1, ZOH>), dim3(tiles, (unsigned)a.B, (unsigned)(nseg - 1)),
+  hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 1, ZOH, FLAGS>), dim3(tiles, (unsigned)a.B, (unsigned)(nseg - 1)),
                      dim3(64 * NW), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -398,7 +399,7 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   hipLaunchKernelGGL(fwd_seg_combine_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, a, nseg);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0, ZOH>), dim3(tiles, (unsigned)a.B, (unsigned)nseg),
+  hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0, ZOH, FLAGS>), dim3(tiles, (unsigned)a.B, (unsigned)nseg),
                      dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
@@ -407,16 +408,18 @@ template <typename IO, int N>
 static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
   constexpr int NPL = N >= 2 ? 2 : 1;
   constexpr int mincpw = 64 * NPL / N > 16 ? 64 * NPL / N : 16;
-  if (a.flags & kFlagZoh)  // one tile width for the exact-hold variant (fewer instantiations)
-    return launch_fwd_cpw<IO, N, (mincpw > 32 ? 64 : 32), true>(a, s);
+  // options use one tile width (fewer instantiations); the plain scan picks its own
+  constexpr int OCPW = mincpw > 32 ? 64 : 32;
+  if (a.flags & kFlagZoh) return launch_fwd_cpw<IO, N, OCPW, true, true>(a, s);
+  if (a.flags) return launch_fwd_cpw<IO, N, OCPW, false, true>(a, s);
   const int cpw = pick_cpw<N>(a);
   if constexpr (mincpw <= 16) {
-    if (cpw == 16) return launch_fwd_cpw<IO, N, 16, false>(a, s);
+    if (cpw == 16) return launch_fwd_cpw<IO, N, 16, false, false>(a, s);
   }
   if constexpr (mincpw <= 32) {
-    if (cpw == 32) return launch_fwd_cpw<IO, N, 32, false>(a, s);
+    if (cpw == 32) return launch_fwd_cpw<IO, N, 32, false, false>(a, s);
   }
-  return launch_fwd_cpw<IO, N, 64, false>(a, s);
+  return launch_fwd_cpw<IO, N, 64, false, false>(a, s);
 }
 
 template <typename IO>

@@ -52,6 +52,10 @@ def _load():
         lib.oracle_state_update.restype = CI
         lib.oracle_state_update_ex.argtypes = lib.oracle_state_update.argtypes + [CI]
         lib.oracle_state_update_ex.restype = CI
+        lib.oracle_conv1d_silu.argtypes = [I, I, I, I, P, P, P, P, P]
+        lib.oracle_conv1d_silu.restype = CI
+        lib.oracle_conv1d_silu_bwd.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
+        lib.oracle_conv1d_silu_bwd.restype = CI
         for f in ("oracle_softplus", "oracle_sigmoid", "oracle_silu"):
             getattr(lib, f).argtypes = [ctypes.c_double]
             getattr(lib, f).restype = ctypes.c_double
@@ -156,6 +160,53 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delt
     if rc != 0:
         raise ValueError(f"oracle_state_update failed ({rc})")
     return st, y
+
+
+def conv1d_silu(x, w, bias=None):
+    """Causal depthwise convolution of width K = w.shape[1] over time, then SiLU.
+    Returns (u, pre), both (B, L, D) fp64."""
+    x, w, bias = _f64(x), _f64(w), _f64(bias)
+    Bsz, L, Dm = x.shape
+    u = np.empty_like(x)
+    pre = np.empty_like(x)
+    rc = _load().oracle_conv1d_silu(Bsz, L, Dm, w.shape[1], _p(x), _p(w), _p(bias), _p(pre), _p(u))
+    if rc != 0:
+        raise ValueError(f"oracle_conv1d_silu failed ({rc})")
+    return u, pre
+
+
+def conv1d_silu_bwd(x, w, bias, du):
+    """Backward of conv1d_silu: returns (dx, dw, dbias or None)."""
+    x, w, bias, du = _f64(x), _f64(w), _f64(bias), _f64(du)
+    Bsz, L, Dm = x.shape
+    dx = np.empty_like(x)
+    dw = np.empty_like(w)
+    db = np.empty(Dm) if bias is not None else None
+    rc = _load().oracle_conv1d_silu_bwd(Bsz, L, Dm, w.shape[1], _p(x), _p(w), _p(bias), _p(du),
+                                        _p(dx), _p(dw), _p(db))
+    if rc != 0:
+        raise ValueError(f"oracle_conv1d_silu_bwd failed ({rc})")
+    return dx, dw, db
+
+
+def scan_fwd_conv(x, conv_w, conv_b, delta, A, B, C, D=None, z=None, delta_bias=None,
+                  delta_softplus=True, h0=None, chunk_len=None, nthreads=None, zoh=False):
+    """The scan fed by the convolution: u = silu(conv(x)), then scan_fwd."""
+    u, _ = conv1d_silu(x, conv_w, conv_b)
+    return scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, chunk_len,
+                    nthreads, zoh=zoh)
+
+
+def scan_bwd_conv(x, conv_w, conv_b, delta, A, B, C, D=None, z=None, delta_bias=None,
+                  delta_softplus=True, h0=None, dy=None, dh_final=None, nthreads=None, zoh=False):
+    """Backward of scan_fwd_conv: the scan gradients with du replaced by dx,
+    plus dconv_w and dconv_b."""
+    u, _ = conv1d_silu(x, conv_w, conv_b)
+    g = scan_bwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, dy, dh_final,
+                 nthreads, zoh=zoh)
+    dx, dw, db = conv1d_silu_bwd(x, conv_w, conv_b, g.pop("du"))
+    g.update(dx=dx, dconv_w=dw, dconv_b=db)
+    return g
 
 
 def softplus(x: float) -> float:

@@ -13,6 +13,7 @@ news page, the D*u skip and SiLU gate of the Mamba block.
 from __future__ import annotations
 
 import numpy as np
+from scipy.signal import lfilter
 from scipy.special import expit
 
 
@@ -160,3 +161,35 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delt
     if z is not None:
         y = y * z * expit(z)
     return new, y
+
+
+def conv1d_silu(x, w, bias=None):
+    """Causal depthwise convolution as an FIR filter along time per channel
+    (``scipy.signal.lfilter`` with taps w[d, ::-1], zero initial conditions),
+    then SiLU.  Returns (u, pre)."""
+    x, w, bias = map(_f64, (x, w, bias))
+    pre = np.empty_like(x)
+    for d in range(x.shape[2]):
+        pre[:, :, d] = lfilter(w[d, ::-1], [1.0], x[:, :, d], axis=1)
+    if bias is not None:
+        pre = pre + bias
+    return pre * expit(pre), pre
+
+
+def conv1d_silu_bwd(x, w, bias, du):
+    """Backward of conv1d_silu: the transposed filter runs backwards in time."""
+    x, w, bias, du = map(_f64, (x, w, bias, du))
+    _, pre = conv1d_silu(x, w, bias)
+    sig = expit(pre)
+    g = du * (sig + pre * sig * (1.0 - sig))
+    K = w.shape[1]
+    dx = np.empty_like(x)
+    for d in range(x.shape[2]):
+        dx[:, :, d] = lfilter(w[d, ::-1], [1.0], g[:, ::-1, d], axis=1)[:, ::-1]
+    L = x.shape[1]
+    dw = np.empty_like(w)
+    for k in range(K):
+        s = K - 1 - k  # tap k reads x shifted by s steps
+        dw[:, k] = np.einsum("bld,bld->d", x[:, :L - s], g[:, s:]) if s < L else 0.0
+    db = g.sum(axis=(0, 1)) if bias is not None else None
+    return dx, dw, db

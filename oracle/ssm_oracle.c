@@ -39,6 +39,12 @@
  *     delta equation broadcasts one value per token over D); ddelta is then
  *     (B,L), the sum over channels.
  *
+ * The causal depthwise convolution of the Mamba block (the Italian overview
+ * article, "Iniziare con Mamba": the block applies a causal Conv1d before the
+ * selective SSM; reading guide, "Temel terimler", Mamba block) is a separate
+ * pair of functions, oracle_conv1d_silu and oracle_conv1d_silu_bwd: per
+ * channel a width-K filter over time with a bias, then SiLU.
+ *
  * Everything is fp64.  Channels (b, d) are independent recurrences; threads
  * split the channels and never reorder the arithmetic inside one channel.
  * Reductions over channels (dB, dC, and over (b, t) for dA, dD, dbias) are
@@ -415,4 +421,72 @@ int oracle_state_update(int64_t B, int64_t D, int64_t N, double *state, const do
                         double *y) {
   return oracle_state_update_ex(B, D, N, state, u, delta, A, Bm, Cm, Dskip, z, delta_bias, softplus, y,
                                 0);
+}
+
+/* ---- causal depthwise convolution + SiLU --------------------------------- */
+
+/* pre[b,t,d] = bias[d] + sum_{k<K} w[d,k] x[b, t-(K-1)+k, d] (x = 0 before the
+ * first step), u = silu(pre).  bias may be NULL (zero); pre or u may be NULL
+ * (not wanted).  Layouts: x, pre, u (B,L,D); w (D,K). */
+int oracle_conv1d_silu(int64_t B, int64_t L, int64_t D, int64_t K, const double *x, const double *w,
+                       const double *bias, double *pre, double *u) {
+  if (B < 1 || L < 1 || D < 1 || K < 1) return -1;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t t = 0; t < L; ++t)
+      for (int64_t d = 0; d < D; ++d) {
+        double acc = bias ? bias[d] : 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+          const int64_t ts = t - (K - 1) + k;
+          if (ts >= 0) acc += w[d * K + k] * x[(b * L + ts) * D + d];
+        }
+        const int64_t i = (b * L + t) * D + d;
+        if (pre) pre[i] = acc;
+        if (u) u[i] = oracle_silu(acc);
+      }
+  return 0;
+}
+
+/* Backward of oracle_conv1d_silu given du = dLoss/du:
+ *   g = du * silu'(pre), silu'(p) = sigmoid(p) (1 + p (1 - sigmoid(p)))
+ *   dx[b,t,d] = sum_k w[d,k] g[b, t+(K-1)-k, d]   (g = 0 past the last step)
+ *   dw[d,k]   = sum_{b,t} x[b, t-(K-1)+k, d] g[b,t,d]
+ *   dbias[d]  = sum_{b,t} g[b,t,d]
+ * dbias may be NULL.  Outputs are overwritten. */
+int oracle_conv1d_silu_bwd(int64_t B, int64_t L, int64_t D, int64_t K, const double *x,
+                           const double *w, const double *bias, const double *du, double *dx,
+                           double *dw, double *dbias) {
+  if (B < 1 || L < 1 || D < 1 || K < 1) return -1;
+  double *g = (double *)malloc(sizeof(double) * (size_t)(B * L * D));
+  if (!g) return -2;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t t = 0; t < L; ++t)
+      for (int64_t d = 0; d < D; ++d) {
+        double p = bias ? bias[d] : 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+          const int64_t ts = t - (K - 1) + k;
+          if (ts >= 0) p += w[d * K + k] * x[(b * L + ts) * D + d];
+        }
+        const double sg = oracle_sigmoid(p);
+        const int64_t i = (b * L + t) * D + d;
+        g[i] = du[i] * sg * (1.0 + p * (1.0 - sg));
+      }
+  for (int64_t i = 0; i < D * K; ++i) dw[i] = 0.0;
+  if (dbias)
+    for (int64_t d = 0; d < D; ++d) dbias[d] = 0.0;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t t = 0; t < L; ++t)
+      for (int64_t d = 0; d < D; ++d) {
+        const int64_t i = (b * L + t) * D + d;
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+          const int64_t tf = t + (K - 1) - k;
+          if (tf < L) acc += w[d * K + k] * g[(b * L + tf) * D + d];
+          const int64_t ts = t - (K - 1) + k;
+          if (ts >= 0) dw[d * K + k] += x[(b * L + ts) * D + d] * g[i];
+        }
+        dx[i] = acc;
+        if (dbias) dbias[d] += g[i];
+      }
+  free(g);
+  return 0;
 }

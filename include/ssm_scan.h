@@ -197,6 +197,52 @@ int ssm_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, 
                     int64_t workspace_bytes, void *hip_stream, int flags);
 
 /*
+ * The scan fed by the causal depthwise convolution of the Mamba block (the
+ * Italian overview article on nisoo.com, "Iniziare con Mamba": the block puts a
+ * causal Conv1d in front of the selective SSM; reading guide, "Temel
+ * terimler", Mamba block), fused so that u never goes to memory:
+ *   pre[b,t,d] = conv_b[d] + sum_{k<K} conv_w[d,k] x[b, t-(K-1)+k, d]
+ *                (x = 0 before the first step; tap K-1 multiplies the
+ *                current step), u = silu(pre) = pre * sigmoid(pre),
+ * then exactly ssm_scan_fwd_ex on u.  x is (B,L,D) in io_dtype; conv_w is
+ * (D,K) fp32 with K = conv_width in 1..4; conv_b (D) fp32 is optional.
+ * flags: SSM_FLAG_ZOH, SSM_FLAG_DELTA_PER_TOKEN, SSM_FLAG_ACCUMULATE
+ * (SSM_FLAG_REVERSE is rejected: the convolution runs forward in time).
+ * Workspace as for ssm_scan_fwd.
+ */
+int ssm_scan_fwd_conv(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                      const void *x, const float *conv_w, const float *conv_b, int conv_width,
+                      const void *delta, const float *A, const void *Bmat, const void *Cmat,
+                      const float *Dskip, const void *z, const float *delta_bias,
+                      int delta_softplus, const float *h0, float *h_final, void *y,
+                      float *chunk_states, void *workspace, int64_t workspace_bytes,
+                      void *hip_stream, int flags);
+
+/* Device workspace ssm_scan_bwd_conv needs.  -1 on invalid sizes. */
+int64_t ssm_scan_bwd_conv_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim,
+                                          int64_t dstate, int io_dtype);
+
+/*
+ * Backward of ssm_scan_fwd_conv.  u is recomputed from x.  Outputs as for
+ * ssm_scan_bwd_ex with du replaced by dx (B,L,D) io_dtype, plus dconv_w (D,K)
+ * fp32 and dconv_b (D) fp32 (required iff conv_b != NULL), all overwritten:
+ *   g = dLoss/du * silu'(pre),  dx[b,t,d] = sum_k conv_w[d,k] g[b, t+(K-1)-k, d],
+ *   dconv_w[d,k] = sum_{b,t} x[b, t-(K-1)+k, d] g[b,t,d],  dconv_b[d] = sum_{b,t} g.
+ * flags: SSM_FLAG_ZOH and SSM_FLAG_DELTA_PER_TOKEN, matching the forward.
+ * Workspace: ssm_scan_bwd_conv_workspace_bytes() bytes.  Sums are in a fixed
+ * order (deterministic).
+ */
+int ssm_scan_bwd_conv(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                      const void *x, const float *conv_w, const float *conv_b, int conv_width,
+                      const void *delta, const float *A, const void *Bmat, const void *Cmat,
+                      const float *Dskip, const void *z, const float *delta_bias,
+                      int delta_softplus, const float *h0, const float *chunk_states,
+                      const void *dy, const float *dh_final, void *dx, float *dconv_w,
+                      float *dconv_b, void *ddelta, float *dA, void *dB, void *dC, float *dD,
+                      void *dz, float *ddelta_bias, float *dh0, void *workspace,
+                      int64_t workspace_bytes, void *hip_stream, int flags);
+
+/*
  * One decode step (reading guide, "Sorular", the question on KV caches: the
  * model keeps a fixed D x N state per layer and advances it one token at a
  * time).  state (B,D,N) fp32 is read once and overwritten in place with the

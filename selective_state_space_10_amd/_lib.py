@@ -13,7 +13,8 @@ SSM_BF16 = 1
 EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_error", "ssm_scan_chunk_len",
            "ssm_scan_chunk_states_bytes", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd",
            "ssm_scan_fwd_ex", "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_ex",
-           "ssm_state_update", "ssm_state_update_ex")
+           "ssm_state_update", "ssm_state_update_ex", "ssm_scan_fwd_conv",
+           "ssm_scan_bwd_conv_workspace_bytes", "ssm_scan_bwd_conv")
 
 # option bits of the *_ex entry points
 FLAG_ZOH = 1
@@ -64,6 +65,16 @@ def load() -> ctypes.CDLL:
         ex = getattr(lib, name + "_ex")
         ex.restype = INT
         ex.argtypes = getattr(lib, name).argtypes + [INT]
+    lib.ssm_scan_fwd_conv.restype = INT
+    lib.ssm_scan_fwd_conv.argtypes = [I64] * 4 + [INT] + [P] * 3 + [INT] + [P] * 7 + [INT] \
+        + [P] * 5 + [I64, P, INT]
+    lib.ssm_scan_bwd_conv_workspace_bytes.restype = I64
+    lib.ssm_scan_bwd_conv_workspace_bytes.argtypes = [I64] * 4 + [INT]
+    lib.ssm_scan_bwd_conv.restype = INT
+    # h0, chunk_states, dy, dh_final, dx, dconv_w, dconv_b, ddelta, dA, dB, dC, dD, dz,
+    # ddelta_bias, dh0, workspace
+    lib.ssm_scan_bwd_conv.argtypes = [I64] * 4 + [INT] + [P] * 3 + [INT] + [P] * 7 + [INT] \
+        + [P] * 16 + [I64, P, INT]
     _lib = lib
     return lib
 

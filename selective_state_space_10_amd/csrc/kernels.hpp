@@ -18,6 +18,9 @@ constexpr int kFlagReverse = 2;       // scan from the last step to the first
 constexpr int kFlagDeltaPerToken = 4; // delta is (B, L), shared by all channels
 constexpr int kFlagAccumulate = 8;    // forward only: y += result instead of y = result
 
+// Widest causal convolution that can be fused in front of the scan.
+constexpr int kMaxConv = 4;
+
 struct FwdArgs {
   int64_t B, L, D, N;
   const void *u, *delta, *Bm, *Cm, *z;
@@ -34,6 +37,10 @@ struct FwdArgs {
   // states entering each segment; all (B, nseg, D[, N]) fp32 in the workspace
   int64_t seg_len;
   float *seg_hloc, *seg_dsum, *seg_state;
+  // causal depthwise convolution + SiLU producing u from x (conv_k = 0: u is given)
+  const void *x;
+  const float *conv_w, *conv_b;
+  int conv_k;
 };
 
 struct BwdArgs {
@@ -46,6 +53,13 @@ struct BwdArgs {
   float *dA, *dD, *dbias, *dh0;
   void *workspace;
   int64_t workspace_bytes;
+  // convolution in front of the scan (conv_k = 0: none): u is recomputed from
+  // x; the outputs are dx (in place of du), dconv_w and dconv_b
+  const void *x;
+  const float *conv_w, *conv_b;
+  int conv_k;
+  void *dx;
+  float *dconv_w, *dconv_b;
 };
 
 struct DecodeArgs {
@@ -60,6 +74,7 @@ struct DecodeArgs {
 
 int64_t fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype);
 int64_t bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype);
+int64_t bwd_conv_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype);
 
 // Each launcher enqueues its kernels on `stream` and returns the first HIP
 // error reported while enqueuing (hipSuccess otherwise).

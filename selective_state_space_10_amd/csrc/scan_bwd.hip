@@ -61,8 +61,12 @@ struct BwdWs {
   float *partD, *partBias;  // (B, nseg, D)
   float *lamloc, *carry;    // (B, nseg, D, N): sequence split only
   float *dsum;              // (B, nseg, D)
-  int64_t ntiles, nseg, seg_len;
+  float *gconv;             // (B, L, D): gradient at the convolution's pre-activation
+  float *cwp, *cbp;         // (B, nrb, D, kMaxConv) and (B, nrb, D): conv tap and bias partials
+  int64_t ntiles, nseg, seg_len, nrb;
 };
+
+constexpr int64_t kConvRows = 256;  // rows per block of the convolution backward
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
@@ -83,8 +87,9 @@ int64_t bwd_split_len(int64_t B, int64_t L, int64_t D) {
   return len;
 }
 
-BwdWs carve_ws(void *base, int64_t B, int64_t L, int64_t D, int64_t N, int64_t *total) {
+BwdWs carve_ws(void *base, int64_t B, int64_t L, int64_t D, int64_t N, int64_t *total, bool conv = false) {
   BwdWs w;
+  w.nrb = (L + kConvRows - 1) / kConvRows;
   w.ntiles = (D + kCPW - 1) / kCPW;
   w.seg_len = bwd_split_len(B, L, D);
   w.nseg = w.seg_len ? (L + w.seg_len - 1) / w.seg_len : 1;
@@ -109,6 +114,13 @@ BwdWs carve_ws(void *base, int64_t B, int64_t L, int64_t D, int64_t N, int64_t *
   } else {
     w.lamloc = w.carry = w.dsum = nullptr;
   }
+  if (conv) {
+    w.gconv = take(B * L * D * 4);
+    w.cwp = take(B * w.nrb * D * kMaxConv * 4);
+    w.cbp = take(B * w.nrb * D * 4);
+  } else {
+    w.gconv = w.cwp = w.cbp = nullptr;
+  }
   if (total) *total = off;
   return w;
 }
@@ -119,9 +131,12 @@ BwdWs carve_ws(void *base, int64_t B, int64_t L, int64_t D, int64_t N, int64_t *
 // blockIdx.z + 1 is the segment.
 // ZOH: the exact zero-order-hold input term coef = expm1(dt A)/A, whose
 // derivatives are d coef/d dt = exp(dt A) and d coef/d A = dt^2 psi(dt A).
+// CONV: u is recomputed as silu(conv(x)) from the causal convolution's input,
+// and the gradient is written at the convolution's pre-activation (the
+// convolution's own backward runs afterwards).
 // Reverse direction and one step size per token are runtime flags; steps are
 // numbered in scan order and mapped to memory rows.
-template <typename IO, int N, int MODE, bool ZOH>
+template <typename IO, int N, int MODE, bool ZOH, bool CONV>
 __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs a, BwdWs ws) {
   constexpr int NPL = N >= 2 ? 2 : 1;  // states per lane
   constexpr int NW = N / NPL;          // waves (state slices)
@@ -167,8 +182,12 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
   const bool rev = (a.flags & kFlagReverse) != 0;
   const bool tok = (a.flags & kFlagDeltaPerToken) != 0;
   auto mrow = [&](int64_t t) { return rev ? L - 1 - t : t; };  // memory row of scan step t
+  constexpr int XK = CONV ? kMaxConv : 1;
+  const int ck = CONV ? a.conv_k : 0;
+  const IO *__restrict__ xin = (const IO *)a.x;
 
   __shared__ __attribute__((aligned(16))) float2 P[T][CPW];  // (dt, dt*u), or (dt, u) with ZOH
+  __shared__ __attribute__((aligned(16))) float SGC[CONV ? T : 1][CPW];  // silu' at the conv output
   __shared__ __attribute__((aligned(16))) float E[T][CPW];   // dy * silu(z)
   __shared__ __attribute__((aligned(16))) float U[T][CPW];   // u
   __shared__ __attribute__((aligned(16))) float SG[T][CPW];  // d dt / d raw delta
@@ -187,6 +206,13 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
   if (a.bias) {
     const float4 v = *(const float4 *)(a.bias + dgc);
     bias4[0] = v.x, bias4[1] = v.y, bias4[2] = v.z, bias4[3] = v.w;
+  }
+  float cw[4][XK], cb4[4] = {0.f, 0.f, 0.f, 0.f};  // convolution taps and bias of the group
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int kk = 0; kk < XK; ++kk) cw[q][kk] = kk < ck ? a.conv_w[(dgc + q) * ck + kk] : 0.0f;
+    if (ck && a.conv_b) cb4[q] = a.conv_b[dgc + q];
   }
 
   // --- sweep ownership: channel d0 + lane, slot s holds state w*NPL + (s ^ par)
@@ -215,6 +241,7 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
   float dD_acc = 0.0f, dbias_acc = 0.0f, dsum = 0.0f;
 
   raw_t r_dl[IPT], r_u[IPT], r_z[IPT], r_dy[IPT];
+  raw_t r_x[IPT][XK];
   float r_b[BPT], r_c[BPT], r_h[NPL];
 
   auto load_chunk = [&](int64_t kc) {
@@ -226,7 +253,16 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
       const int64_t idx = r * D + dgc;
       r_dl[j] = tok ? V::splat(dl, r) : V::load(dl, idx);
       r_dy[j] = V::load(dyp, idx);
-      if (MODE == 0) r_u[j] = V::load(u, idx);
+      if (MODE == 0 && CONV) {  // the rows the causal convolution reads (forward direction only)
+        const int64_t tm = t < te ? t : te - 1;
+#pragma unroll
+        for (int kk = 0; kk < XK; ++kk) {
+          const int64_t ts = tm - (ck - 1) + kk;
+          r_x[j][kk] = (kk < ck && ts >= 0) ? V::load(xin, (row0 + ts) * D + dgc) : raw_t{};
+        }
+      } else if (MODE == 0) {
+        r_u[j] = V::load(u, idx);
+      }
       if (has_z) r_z[j] = V::load(zz, idx);
     }
 #pragma unroll
@@ -253,7 +289,29 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
       const int tl = tl0 + j * (NT / G);
       const bool ok = gv && t0 + tl < te;  // padding steps and channels: dt = 0, e = 0
       const float4 r4 = V::cvt(r_dl[j]), g4 = V::cvt(r_dy[j]);
-      const float4 x4 = MODE == 0 ? V::cvt(r_u[j]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 x4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (MODE == 0 && CONV) {  // u = silu(pre), pre = bias + sum_k w_k x[t - (K-1) + k]; keep silu'(pre)
+        float pre[4] = {cb4[0], cb4[1], cb4[2], cb4[3]};
+#pragma unroll
+        for (int kk = 0; kk < XK; ++kk) {
+          const float4 xv = V::cvt(r_x[j][kk]);
+          pre[0] = fmaf(cw[0][kk], xv.x, pre[0]);
+          pre[1] = fmaf(cw[1][kk], xv.y, pre[1]);
+          pre[2] = fmaf(cw[2][kk], xv.z, pre[2]);
+          pre[3] = fmaf(cw[3][kk], xv.w, pre[3]);
+        }
+        float uv[4], sd[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float sg = sigmoid_f(pre[q]);
+          uv[q] = pre[q] * sg;
+          sd[q] = sg * fmaf(pre[q], 1.0f - sg, 1.0f);
+        }
+        x4 = make_float4(uv[0], uv[1], uv[2], uv[3]);
+        *(float4 *)&SGC[CONV ? tl : 0][4 * g] = make_float4(sd[0], sd[1], sd[2], sd[3]);
+      } else if (MODE == 0) {
+        x4 = V::cvt(r_u[j]);
+      }
       const float4 z4 = has_z ? V::cvt(r_z[j]) : make_float4(0.f, 0.f, 0.f, 0.f);
       const float rv[4] = {r4.x, r4.y, r4.z, r4.w}, gv4[4] = {g4.x, g4.y, g4.z, g4.w};
       const float xv[4] = {x4.x, x4.y, x4.z, x4.w}, zv[4] = {z4.x, z4.y, z4.z, z4.w};
@@ -354,7 +412,11 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
         // with ZOH the sweep already folded the input-coefficient terms in
         ddl = (ZOH ? dda : fmaf(x, dua, dda)) * SG[tl][lane];
         const int64_t idx = (row0 + mrow(t)) * D + d;
-        store_io((IO *)a.du, idx, fmaf(Dv, e, ZOH ? dua : dt * dua));
+        const float du = fmaf(Dv, e, ZOH ? dua : dt * dua);
+        if (CONV)  // chain through the SiLU; the convolution's backward reads it
+          ws.gconv[idx] = du * SGC[CONV ? tl : 0][lane];
+        else
+          store_io((IO *)a.du, idx, du);
         if (!tok) store_io((IO *)a.ddelta, idx, ddl);
         if (has_z) store_io((IO *)a.dz, idx, GZ[tl][lane] * fmaf(Dv, x, pre));
         dD_acc = fmaf(e, x, dD_acc);
@@ -541,6 +603,71 @@ __global__ void __launch_bounds__(256) bwd_reduce_tok_kernel(BwdArgs a, BwdWs ws
   }
 }
 
+// Backward of the causal convolution from the gradient g at its pre-activation:
+//   dx[b,t,d] = sum_k w[d,k] g[b, t+(K-1)-k, d],
+//   dw[d,k] += x[b, t-(K-1)+k, d] g[b,t,d],   dbias[d] += g[b,t,d].
+// Taps are padded at the front to width kMaxConv (zero taps), so the windows
+// are static.  One thread per (channel, batch row, block of kConvRows rows);
+// tap and bias sums are per-block partials.
+template <typename IO>
+__global__ void __launch_bounds__(256) conv_bwd_kernel(BwdArgs a, BwdWs ws) {
+  constexpr int W = kMaxConv;
+  const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t b = blockIdx.y, rb = blockIdx.z;
+  const int64_t L = a.L, D = a.D;
+  if (d >= D) return;  // no barrier in this kernel
+  const int K = a.conv_k;
+  float wp[W];  // padded taps: wp[k'] = w[k' - (W - K)] for k' >= W - K
+#pragma unroll
+  for (int k = 0; k < W; ++k) wp[k] = k >= W - K ? a.conv_w[d * K + k - (W - K)] : 0.0f;
+  const IO *xin = (const IO *)a.x;
+  const float *g = ws.gconv;
+  const int64_t t0 = rb * kConvRows, t1 = t0 + kConvRows < L ? t0 + kConvRows : L;
+  const int64_t base = b * L;
+  float gw[W], xw[W];  // gw[j] = g[t + j], xw[k'] = x[t - (W-1) + k']
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    gw[j] = t0 + j < L ? g[(base + t0 + j) * D + d] : 0.0f;
+    const int64_t ts = t0 - (W - 1) + j;
+    xw[j] = ts >= 0 ? load_io(xin, (base + ts) * D + d) : 0.0f;
+  }
+  float dwp[W] = {0.f, 0.f, 0.f, 0.f}, db = 0.0f;
+  for (int64_t t = t0; t < t1; ++t) {
+    float dxv = 0.0f;
+#pragma unroll
+    for (int j = 0; j < W; ++j) dxv = fmaf(wp[W - 1 - j], gw[j], dxv);
+    store_io((IO *)a.dx, (base + t) * D + d, dxv);
+#pragma unroll
+    for (int k = 0; k < W; ++k) dwp[k] = fmaf(xw[k], gw[0], dwp[k]);
+    db += gw[0];
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) gw[j] = gw[j + 1], xw[j] = xw[j + 1];
+    gw[W - 1] = t + W < L ? g[(base + t + W) * D + d] : 0.0f;
+    xw[W - 1] = t + 1 < L ? load_io(xin, (base + t + 1) * D + d) : 0.0f;
+  }
+  const int64_t pi = (b * ws.nrb + rb) * D + d;
+#pragma unroll
+  for (int k = 0; k < W; ++k) ws.cwp[pi * W + k] = dwp[k];
+  ws.cbp[pi] = db;
+}
+
+// Convolution taps and bias: sum of the per-block partials in a fixed order.
+__global__ void __launch_bounds__(256) conv_reduce_kernel(BwdArgs a, BwdWs ws) {
+  constexpr int W = kMaxConv;
+  const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (d >= a.D) return;
+  const int K = a.conv_k;
+  const int64_t R = a.B * ws.nrb;
+  float sw[W] = {0.f, 0.f, 0.f, 0.f}, sb = 0.0f;
+  for (int64_t r = 0; r < R; ++r) {
+#pragma unroll
+    for (int k = 0; k < W; ++k) sw[k] += ws.cwp[(r * a.D + d) * W + k];
+    sb += ws.cbp[r * a.D + d];
+  }
+  for (int k = 0; k < K; ++k) a.dconv_w[d * K + k] = sw[k + W - K];
+  if (a.dconv_b) a.dconv_b[d] = sb;
+}
+
 // dA, dD, d bias: sum of the partials over batch rows and segments.
 __global__ void __launch_bounds__(256) bwd_reduce_params_kernel(BwdArgs a, BwdWs ws) {
   const int64_t DN = a.D * a.N;
@@ -565,24 +692,36 @@ __global__ void __launch_bounds__(256) bwd_reduce_params_kernel(BwdArgs a, BwdWs
 template <typename IO, int N>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
   constexpr int NT = 64 * (N >= 2 ? N / 2 : 1);
-  BwdWs ws = carve_ws(a.workspace, a.B, a.L, a.D, a.N, nullptr);
+  const bool conv = a.conv_k > 0;
+  BwdWs ws = carve_ws(a.workspace, a.B, a.L, a.D, a.N, nullptr, conv);
   const unsigned tiles = (unsigned)ws.ntiles;
   hipError_t e;
   if (ws.seg_len) {
-    hipLaunchKernelGGL((bwd_kernel<IO, N, 1, false>), dim3(tiles, (unsigned)a.B, (unsigned)(ws.nseg - 1)), dim3(NT), 0, s,
+    hipLaunchKernelGGL((bwd_kernel<IO, N, 1, false, false>), dim3(tiles, (unsigned)a.B, (unsigned)(ws.nseg - 1)), dim3(NT), 0, s,
                        a, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nst = a.B * a.D * a.N;
     hipLaunchKernelGGL(bwd_seg_combine_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, a, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (a.flags & kFlagZoh)
-    hipLaunchKernelGGL((bwd_kernel<IO, N, 0, true>), dim3(tiles, (unsigned)a.B, (unsigned)ws.nseg), dim3(NT), 0, s, a,
-                       ws);
+  const dim3 grid(tiles, (unsigned)a.B, (unsigned)ws.nseg);
+  const bool zoh = (a.flags & kFlagZoh) != 0;
+  if (zoh && conv)
+    hipLaunchKernelGGL((bwd_kernel<IO, N, 0, true, true>), grid, dim3(NT), 0, s, a, ws);
+  else if (zoh)
+    hipLaunchKernelGGL((bwd_kernel<IO, N, 0, true, false>), grid, dim3(NT), 0, s, a, ws);
+  else if (conv)
+    hipLaunchKernelGGL((bwd_kernel<IO, N, 0, false, true>), grid, dim3(NT), 0, s, a, ws);
   else
-    hipLaunchKernelGGL((bwd_kernel<IO, N, 0, false>), dim3(tiles, (unsigned)a.B, (unsigned)ws.nseg), dim3(NT), 0, s, a,
-                       ws);
+    hipLaunchKernelGGL((bwd_kernel<IO, N, 0, false, false>), grid, dim3(NT), 0, s, a, ws);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (conv) {
+    const unsigned dt = (unsigned)((a.D + 255) / 256);
+    hipLaunchKernelGGL((conv_bwd_kernel<IO>), dim3(dt, (unsigned)a.B, (unsigned)ws.nrb), dim3(256), 0, s, a, ws);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(conv_reduce_kernel, dim3(dt), dim3(256), 0, s, a, ws);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (a.flags & kFlagDeltaPerToken) {
     int64_t tb = (a.B * a.L + 255) / 256;
     if (tb > 65536) tb = 65536;
@@ -615,6 +754,12 @@ hipError_t launch_bwd_io(const BwdArgs &a, hipStream_t s) {
 int64_t bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int) {
   int64_t total = 0;
   carve_ws(nullptr, B, L, D, N, &total);
+  return total;
+}
+
+int64_t bwd_conv_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int) {
+  int64_t total = 0;
+  carve_ws(nullptr, B, L, D, N, &total, true);
   return total;
 }
 

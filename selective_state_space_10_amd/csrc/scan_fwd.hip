@@ -79,6 +79,9 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
   const bool rev = FLAGS && (a.flags & kFlagReverse) != 0;
   const bool tok = FLAGS && (a.flags & kFlagDeltaPerToken) != 0;
   const bool accum = FLAGS && (a.flags & kFlagAccumulate) != 0;
+  const int ck = FLAGS ? a.conv_k : 0;  // width of the causal convolution producing u (0: u given)
+  const IO *__restrict__ xin = (const IO *)a.x;
+  constexpr int XK = FLAGS ? kMaxConv : 1;
   auto mrow = [&](int64_t t) { return rev ? L - 1 - t : t; };  // memory row of scan step t
 
   __shared__ __attribute__((aligned(16))) float2 P[T][CPW];  // (dt, dt*u), or (dt, u) with ZOH
@@ -99,6 +102,13 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
   if (a.Dskip) {
     const float4 v = *(const float4 *)(a.Dskip + dgc);
     Dsk4[0] = v.x, Dsk4[1] = v.y, Dsk4[2] = v.z, Dsk4[3] = v.w;
+  }
+  float cw[4][XK], cb4[4] = {0.f, 0.f, 0.f, 0.f};  // convolution taps and bias of the group
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int kk = 0; kk < XK; ++kk) cw[q][kk] = kk < ck ? a.conv_w[(dgc + q) * ck + kk] : 0.0f;
+    if (ck && a.conv_b) cb4[q] = a.conv_b[dgc + q];
   }
 
   // --- recurrence ownership: channel d0 + c, state slice spi = w*NG + gi
@@ -125,18 +135,28 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
   }
 
   raw_t r_raw[PD][IPT], r_u[PD][IPT], r_z[PD][IPT];  // loads in flight
+  raw_t r_x[PD][IPT][XK];                              // convolution input rows
   float r_b[PD][BPT], r_c[PD][BPT];
   float4 keep_u[IPT], keep_g[IPT];                     // kept for the epilogue
 
   auto load_chunk = [&](int64_t k, raw_t(&ra)[IPT], raw_t(&ru)[IPT], raw_t(&rz)[IPT], float(&rb)[BPT],
-                        float(&rc)[BPT]) {
+                        float(&rc)[BPT], raw_t(&rx)[IPT][XK]) {
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int64_t t = tb + k * T + tl0 + j * (NT / G);
       const int64_t r = row0 + mrow(t < te ? t : te - 1);
       const int64_t idx = r * D + dgc;
       ra[j] = tok ? V::splat(dl, r) : V::load(dl, idx);
-      ru[j] = V::load(u, idx);
+      if (ck) {  // the rows the causal convolution reads (forward direction only)
+        const int64_t tm = t < te ? t : te - 1;
+#pragma unroll
+        for (int kk = 0; kk < XK; ++kk) {
+          const int64_t ts = tm - (ck - 1) + kk;
+          rx[j][kk] = (kk < ck && ts >= 0) ? V::load(xin, (row0 + ts) * D + dgc) : raw_t{};
+        }
+      } else {
+        ru[j] = V::load(u, idx);
+      }
       if (has_z) rz[j] = V::load(zz, idx);
     }
 #pragma unroll
@@ -151,12 +171,27 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
     }
   };
   auto prologue = [&](int64_t k, raw_t(&ra)[IPT], raw_t(&ru)[IPT], raw_t(&rz)[IPT], float(&rb)[BPT],
-                      float(&rc)[BPT]) {
+                      float(&rc)[BPT], raw_t(&rx)[IPT][XK]) {
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int tl = tl0 + j * (NT / G);
       const bool tv = tb + k * T + tl < te;  // steps past the end get dt = 0: no state change
-      const float4 r = V::cvt(ra[j]), x = V::cvt(ru[j]);
+      const float4 r = V::cvt(ra[j]);
+      float4 x;
+      if (ck) {  // u = silu(bias + sum_k w_k x[t - (K-1) + k])
+        float pre[4] = {cb4[0], cb4[1], cb4[2], cb4[3]};
+#pragma unroll
+        for (int kk = 0; kk < XK; ++kk) {
+          const float4 xv = V::cvt(rx[j][kk]);
+          pre[0] = fmaf(cw[0][kk], xv.x, pre[0]);
+          pre[1] = fmaf(cw[1][kk], xv.y, pre[1]);
+          pre[2] = fmaf(cw[2][kk], xv.z, pre[2]);
+          pre[3] = fmaf(cw[3][kk], xv.w, pre[3]);
+        }
+        x = make_float4(silu_f(pre[0]), silu_f(pre[1]), silu_f(pre[2]), silu_f(pre[3]));
+      } else {
+        x = V::cvt(ru[j]);
+      }
       const float rv[4] = {r.x, r.y, r.z, r.w}, xv[4] = {x.x, x.y, x.z, x.w};
       float dt[4];
 #pragma unroll
@@ -273,8 +308,8 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
   // Prime the pipeline: chunks 0 .. PD-1 in flight, prologue of chunk 0.
 #pragma unroll
   for (int s = 0; s < PD; ++s)
-    if (s < nck) load_chunk(s, r_raw[s], r_u[s], r_z[s], r_b[s], r_c[s]);
-  prologue(0, r_raw[0], r_u[0], r_z[0], r_b[0], r_c[0]);
+    if (s < nck) load_chunk(s, r_raw[s], r_u[s], r_z[s], r_b[s], r_c[s], r_x[s]);
+  prologue(0, r_raw[0], r_u[0], r_z[0], r_b[0], r_c[0], r_x[0]);
   __syncthreads();
   // Chunk k uses ring slot k % PD; the loop is unrolled by PD so slots are
   // compile-time register arrays.
@@ -283,12 +318,12 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
     for (int s = 0; s < PD; ++s) {
       const int64_t k = k0 + s;
       if (k < nck) {
-        if (k + PD < nck) load_chunk(k + PD, r_raw[s], r_u[s], r_z[s], r_b[s], r_c[s]);
+        if (k + PD < nck) load_chunk(k + PD, r_raw[s], r_u[s], r_z[s], r_b[s], r_c[s], r_x[s]);
         scan_chunk(k);
         __syncthreads();
         if (MODE == 0) epilogue(k);
         const int sn = (s + 1) % PD;
-        if (k + 1 < nck) prologue(k + 1, r_raw[sn], r_u[sn], r_z[sn], r_b[sn], r_c[sn]);
+        if (k + 1 < nck) prologue(k + 1, r_raw[sn], r_u[sn], r_z[sn], r_b[sn], r_c[sn], r_x[sn]);
         __syncthreads();
       }
     }
@@ -411,7 +446,7 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
   // options use one tile width (fewer instantiations); the plain scan picks its own
   constexpr int OCPW = mincpw > 32 ? 64 : 32;
   if (a.flags & kFlagZoh) return launch_fwd_cpw<IO, N, OCPW, true, true>(a, s);
-  if (a.flags) return launch_fwd_cpw<IO, N, OCPW, false, true>(a, s);
+  if (a.flags || a.conv_k) return launch_fwd_cpw<IO, N, OCPW, false, true>(a, s);
   const int cpw = pick_cpw<N>(a);
   if constexpr (mincpw <= 16) {
     if (cpw == 16) return launch_fwd_cpw<IO, N, 16, false, false>(a, s);

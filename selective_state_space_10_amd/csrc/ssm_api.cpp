@@ -141,6 +141,43 @@ int ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, 
   return hip_status(ssm::launch_fwd(a, io_dtype, (hipStream_t)hip_stream), "ssm_scan_fwd launch");
 }
 
+int ssm_scan_fwd_conv(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                      const void *x, const float *conv_w, const float *conv_b, int conv_width,
+                      const void *delta, const float *A, const void *Bmat, const void *Cmat,
+                      const float *Dskip, const void *z, const float *delta_bias,
+                      int delta_softplus, const float *h0, float *h_final, void *y,
+                      float *chunk_states, void *workspace, int64_t workspace_bytes,
+                      void *hip_stream, int flags) {
+  g_last_error[0] = 0;
+  int st = check_sizes(batch, seqlen, dim, dstate, io_dtype);
+  if (st != SSM_OK) return st;
+  if (flags & ~(SSM_FLAG_ZOH | SSM_FLAG_DELTA_PER_TOKEN | SSM_FLAG_ACCUMULATE))
+    return fail(SSM_ERR_UNSUPPORTED, "flags 0x%x: the fused convolution runs forward in time only", flags);
+  if (conv_width < 1 || conv_width > ssm::kMaxConv)
+    return fail(SSM_ERR_UNSUPPORTED, "conv_width=%d not in 1..%d", conv_width, ssm::kMaxConv);
+  const Ptr ps[] = {{"x", x, true},         {"conv_w", conv_w, true}, {"delta", delta, true},
+                    {"A", A, true},         {"Bmat", Bmat, true},     {"Cmat", Cmat, true},
+                    {"y", y, true},         {"conv_b", conv_b, false}, {"Dskip", Dskip, false},
+                    {"z", z, false},        {"delta_bias", delta_bias, false}, {"h0", h0, false},
+                    {"h_final", h_final, false}, {"chunk_states", chunk_states, false},
+                    {"workspace", workspace, false}};
+  st = check_ptrs(ps, (int)(sizeof(ps) / sizeof(ps[0])));
+  if (st != SSM_OK) return st;
+  const int64_t need = ssm::fwd_workspace_bytes(batch, seqlen, dim, dstate, io_dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(SSM_ERR_WORKSPACE, "forward needs %lld workspace bytes, got %lld", (long long)need,
+                (long long)(workspace ? workspace_bytes : 0));
+  ssm::FwdArgs a{};
+  a.B = batch, a.L = seqlen, a.D = dim, a.N = dstate;
+  a.u = nullptr, a.delta = delta, a.Bm = Bmat, a.Cm = Cmat, a.z = z;
+  a.A = A, a.Dskip = Dskip, a.bias = delta_bias, a.h0 = h0;
+  a.softplus = delta_softplus != 0, a.flags = flags;
+  a.h_final = h_final, a.y = y, a.chunk_states = chunk_states;
+  a.workspace = workspace, a.workspace_bytes = workspace_bytes;
+  a.x = x, a.conv_w = conv_w, a.conv_b = conv_b, a.conv_k = conv_width;
+  return hip_status(ssm::launch_fwd(a, io_dtype, (hipStream_t)hip_stream), "ssm_scan_fwd_conv launch");
+}
+
 int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
                  const void *u, const void *delta, const float *A, const void *Bmat,
                  const void *Cmat, const float *Dskip, const void *z, const float *delta_bias,
@@ -205,6 +242,62 @@ int ssm_scan_bwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, 
   a.dA = dA, a.dD = dD, a.dbias = ddelta_bias, a.dh0 = dh0;
   a.workspace = workspace, a.workspace_bytes = workspace_bytes;
   return hip_status(ssm::launch_bwd(a, io_dtype, (hipStream_t)hip_stream), "ssm_scan_bwd launch");
+}
+
+int64_t ssm_scan_bwd_conv_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                          int io_dtype) {
+  if (check_sizes(batch, seqlen, dim, dstate, io_dtype) != SSM_OK) return -1;
+  return ssm::bwd_conv_workspace_bytes(batch, seqlen, dim, dstate, io_dtype);
+}
+
+int ssm_scan_bwd_conv(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                      const void *x, const float *conv_w, const float *conv_b, int conv_width,
+                      const void *delta, const float *A, const void *Bmat, const void *Cmat,
+                      const float *Dskip, const void *z, const float *delta_bias,
+                      int delta_softplus, const float *h0, const float *chunk_states,
+                      const void *dy, const float *dh_final, void *dx, float *dconv_w,
+                      float *dconv_b, void *ddelta, float *dA, void *dB, void *dC, float *dD,
+                      void *dz, float *ddelta_bias, float *dh0, void *workspace,
+                      int64_t workspace_bytes, void *hip_stream, int flags) {
+  g_last_error[0] = 0;
+  int st = check_sizes(batch, seqlen, dim, dstate, io_dtype);
+  if (st != SSM_OK) return st;
+  if (flags & ~(SSM_FLAG_ZOH | SSM_FLAG_DELTA_PER_TOKEN))
+    return fail(SSM_ERR_UNSUPPORTED, "flags 0x%x not supported with the fused convolution backward", flags);
+  if (conv_width < 1 || conv_width > ssm::kMaxConv)
+    return fail(SSM_ERR_UNSUPPORTED, "conv_width=%d not in 1..%d", conv_width, ssm::kMaxConv);
+  const Ptr ps[] = {{"x", x, true},           {"conv_w", conv_w, true},    {"delta", delta, true},
+                    {"A", A, true},           {"Bmat", Bmat, true},        {"Cmat", Cmat, true},
+                    {"chunk_states", chunk_states, true}, {"dy", dy, true}, {"dx", dx, true},
+                    {"dconv_w", dconv_w, true}, {"ddelta", ddelta, true},  {"dA", dA, true},
+                    {"dB", dB, true},         {"dC", dC, true},            {"workspace", workspace, true},
+                    {"conv_b", conv_b, false}, {"dconv_b", dconv_b, false}, {"Dskip", Dskip, false},
+                    {"z", z, false},          {"delta_bias", delta_bias, false}, {"h0", h0, false},
+                    {"dh_final", dh_final, false}, {"dD", dD, false},      {"dz", dz, false},
+                    {"ddelta_bias", ddelta_bias, false}, {"dh0", dh0, false}};
+  st = check_ptrs(ps, (int)(sizeof(ps) / sizeof(ps[0])));
+  if (st != SSM_OK) return st;
+  if ((conv_b == nullptr) != (dconv_b == nullptr))
+    return fail(SSM_ERR_NULL_ARG, "dconv_b must be given if and only if conv_b is");
+  if ((Dskip == nullptr) != (dD == nullptr))
+    return fail(SSM_ERR_NULL_ARG, "dD must be given if and only if Dskip is");
+  if ((z == nullptr) != (dz == nullptr))
+    return fail(SSM_ERR_NULL_ARG, "dz must be given if and only if z is");
+  const int64_t need = ssm::bwd_conv_workspace_bytes(batch, seqlen, dim, dstate, io_dtype);
+  if (workspace_bytes < need)
+    return fail(SSM_ERR_WORKSPACE, "backward with convolution needs %lld workspace bytes, got %lld",
+                (long long)need, (long long)workspace_bytes);
+  ssm::BwdArgs a{};
+  a.B = batch, a.L = seqlen, a.D = dim, a.N = dstate;
+  a.u = nullptr, a.delta = delta, a.Bm = Bmat, a.Cm = Cmat, a.z = z, a.dy = dy;
+  a.A = A, a.Dskip = Dskip, a.bias = delta_bias, a.h0 = h0, a.chunk_states = chunk_states;
+  a.dh_final = dh_final, a.softplus = delta_softplus != 0, a.flags = flags;
+  a.du = nullptr, a.ddelta = ddelta, a.dB = dB, a.dC = dC, a.dz = dz;
+  a.dA = dA, a.dD = dD, a.dbias = ddelta_bias, a.dh0 = dh0;
+  a.workspace = workspace, a.workspace_bytes = workspace_bytes;
+  a.x = x, a.conv_w = conv_w, a.conv_b = conv_b, a.conv_k = conv_width;
+  a.dx = dx, a.dconv_w = dconv_w, a.dconv_b = dconv_b;
+  return hip_status(ssm::launch_bwd(a, io_dtype, (hipStream_t)hip_stream), "ssm_scan_bwd_conv launch");
 }
 
 int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,

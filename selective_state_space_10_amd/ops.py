@@ -154,6 +154,86 @@ def scan_bwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, chunk_stat
     return g
 
 
+def _check_conv(x, conv_w, conv_b, dev):
+    if not isinstance(conv_w, torch.Tensor) or conv_w.dim() != 2:
+        raise ValueError("conv_w must be a (dim, width) tensor")
+    Dm, K = conv_w.shape
+    if not 1 <= K <= 4:
+        raise ValueError(f"convolution width {K} not in 1..4")
+    _need("conv_w", conv_w, (Dm, K), torch.float32, dev)
+    _need("conv_b", conv_b, (Dm,), torch.float32, dev, optional=True)
+    return K
+
+
+def scan_fwd_conv(x, conv_w, conv_b, delta, A, B, C, D=None, z=None, delta_bias=None,
+                  delta_softplus=True, h0=None, return_final_state=False, save_chunk_states=False,
+                  zoh=False, out=None):
+    """The scan fed by the fused causal depthwise convolution:
+    u = silu(conv_b + sum_k conv_w[:, k] x[t - (K-1) + k]), then scan_fwd on u
+    (u is never written to memory).  Returns (y, h_final or None, chunk_states or None)."""
+    Bsz, L, Dm, N = _check_common(x, delta, A, B, C, D, z, delta_bias, h0)
+    K = _check_conv(x, conv_w, conv_b, x.device)
+    lib = _lib.load()
+    io = _io_code(x)
+    dev = x.device
+    if out is not None:
+        _need("out", out, (Bsz, L, Dm), x.dtype, dev)
+        y = out
+    else:
+        y = torch.empty_like(x)
+    flags = _flags(delta, x, zoh, False, accumulate=out is not None)
+    hf = torch.empty((Bsz, Dm, N), dtype=torch.float32, device=dev) if return_final_state else None
+    cs = None
+    if save_chunk_states:
+        cs = torch.empty((Bsz, -(-L // chunk_len()), N, Dm), dtype=torch.float32, device=dev)
+    wsb = int(lib.ssm_scan_fwd_workspace_bytes(Bsz, L, Dm, N, io))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb > 0 else None
+    with torch.cuda.device(dev):
+        st = lib.ssm_scan_fwd_conv(Bsz, L, Dm, N, io, _ptr(x), _ptr(conv_w), _ptr(conv_b), K,
+                                   _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                   _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(hf),
+                                   _ptr(y), _ptr(cs), _ptr(ws), wsb, _stream(dev), flags)
+    _lib.check(st)
+    return y, hf, cs
+
+
+def scan_bwd_conv(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, delta_softplus, h0,
+                  chunk_states, dy, dh_final=None, want_ddelta_bias=True, want_dh0=True, zoh=False):
+    """Backward of scan_fwd_conv.  Returns a dict: dx, dconv_w, dconv_b, ddelta, dA, dB, dC,
+    dD, dz, ddelta_bias, dh0."""
+    Bsz, L, Dm, N = _check_common(x, delta, A, B, C, D, z, delta_bias, h0)
+    K = _check_conv(x, conv_w, conv_b, x.device)
+    lib = _lib.load()
+    io = _io_code(x)
+    dev = x.device
+    _need("chunk_states", chunk_states, (Bsz, -(-L // chunk_len()), N, Dm), torch.float32, dev)
+    _need("dy", dy, (Bsz, L, Dm), x.dtype, dev)
+    _need("dh_final", dh_final, (Bsz, Dm, N), torch.float32, dev, optional=True)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dx=torch.empty_like(x), dconv_w=torch.empty((Dm, K), **f32),
+             dconv_b=torch.empty((Dm,), **f32) if conv_b is not None else None,
+             ddelta=torch.empty_like(delta), dA=torch.empty((Dm, N), **f32),
+             dB=torch.empty_like(B), dC=torch.empty_like(C),
+             dD=torch.empty((Dm,), **f32) if D is not None else None,
+             dz=torch.empty_like(x) if z is not None else None,
+             ddelta_bias=torch.empty((Dm,), **f32) if (delta_bias is not None and want_ddelta_bias)
+             else None,
+             dh0=torch.empty((Bsz, Dm, N), **f32) if want_dh0 else None)
+    wsb = int(lib.ssm_scan_bwd_conv_workspace_bytes(Bsz, L, Dm, N, io))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = lib.ssm_scan_bwd_conv(Bsz, L, Dm, N, io, _ptr(x), _ptr(conv_w), _ptr(conv_b), K,
+                                   _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                   _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0),
+                                   _ptr(chunk_states), _ptr(dy), _ptr(dh_final), _ptr(g["dx"]),
+                                   _ptr(g["dconv_w"]), _ptr(g["dconv_b"]), _ptr(g["ddelta"]),
+                                   _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
+                                   _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), _ptr(ws),
+                                   wsb, _stream(dev), _flags(delta, x, zoh))
+    _lib.check(st)
+    return g
+
+
 def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
                  zoh=False):
     """One decode step; ``state`` (batch, dim, dstate) fp32 is updated in place.  Returns y.
@@ -228,3 +308,34 @@ def bidirectional_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     y, _, _ = scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, zoh=zoh)
     scan_fwd(u, delta, A, B, C, None, z, delta_bias, delta_softplus, zoh=zoh, reverse=True, out=y)
     return y
+
+
+class ConvScanFn(torch.autograd.Function):
+    """Autograd wrapper of the scan fed by the fused causal convolution."""
+
+    @staticmethod
+    def forward(ctx, x, conv_w, conv_b, delta, A, B, C, D=None, z=None, delta_bias=None,
+                delta_softplus=True, h0=None, zoh=False):
+        y, hf, cs = scan_fwd_conv(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias,
+                                  delta_softplus, h0, return_final_state=True,
+                                  save_chunk_states=True, zoh=zoh)
+        ctx.delta_softplus, ctx.zoh = bool(delta_softplus), bool(zoh)
+        ctx.save_for_backward(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, h0, cs)
+        return y, hf
+
+    @staticmethod
+    def backward(ctx, dy, dhf):
+        x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, h0, cs = ctx.saved_tensors
+        g = scan_bwd_conv(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, ctx.delta_softplus,
+                          h0, cs, dy.contiguous(), None if dhf is None else dhf.contiguous(),
+                          want_ddelta_bias=delta_bias is not None, want_dh0=h0 is not None,
+                          zoh=ctx.zoh)
+        return (g["dx"], g["dconv_w"], g["dconv_b"], g["ddelta"], g["dA"], g["dB"], g["dC"],
+                g["dD"], g["dz"], g["ddelta_bias"], None, g["dh0"], None)
+
+
+def conv_selective_scan(x, conv_w, conv_b, delta, A, B, C, D=None, z=None, delta_bias=None,
+                        delta_softplus=True, h0=None, zoh=False):
+    """Differentiable scan behind the fused causal convolution; returns (y, h_final)."""
+    return ConvScanFn.apply(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                            h0, zoh)

@@ -38,6 +38,16 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_binding_signatures_match_the_header(lib):
+    """Each ctypes prototype has as many arguments as the header declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    protos = re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text)
+    assert len(protos) == len(_declared())
+    for name, params in protos:
+        n = 0 if params.strip() in ("", "void") else len(params.split(","))
+        assert len(getattr(lib, name).argtypes) == n, name
+
+
 def test_version_and_queries(lib):
     assert lib.ssm_abi_version() == 2
     T = lib.ssm_scan_chunk_len()
@@ -138,6 +148,12 @@ def test_option_flags_are_validated(lib):
     assert lib.ssm_state_update_ex(*dargs, 2) == UNSUPPORTED  # no direction for one token
     assert lib.ssm_state_update_ex(*dargs, 4) == UNSUPPORTED
     assert b"SSM_FLAG_ZOH" in lib.ssm_last_error()
+    cargs = (1, 16, 8, 4, 0, FAKE, FAKE, None)
+    rest = (FAKE, FAKE, FAKE, FAKE, None, None, None, 1, None, None, FAKE, None, None, 0, None)
+    assert lib.ssm_scan_fwd_conv(*cargs, 4, *rest, 2) == UNSUPPORTED  # no reverse with the conv
+    assert lib.ssm_scan_fwd_conv(*cargs, 5, *rest, 0) == UNSUPPORTED  # width above 4
+    assert lib.ssm_scan_fwd_conv(*cargs, 0, *rest, 0) == UNSUPPORTED
+    assert lib.ssm_scan_fwd_conv(1, 16, 8, 4, 0, FAKE, None, None, 4, *rest, 0) == NULL_ARG
 
 
 def test_last_error_is_thread_local(lib):

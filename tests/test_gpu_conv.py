@@ -1,0 +1,144 @@
+"""HIP path with the fused causal depthwise convolution in front of the scan
+against the fp64 oracle (the oracle's convolution followed by its scan),
+element by element, through the C ABI.  Tolerances as for the plain path."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+from oracle import oracle_c
+from tests.helpers import nmax_err
+from tests.test_gpu_parity import TOL, _oracle_kwargs, _problem, _to
+from workloads import WORKLOADS, conv_inputs, cotangent, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dx", "dconv_w", "dconv_b", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias", "dh0")
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_10_amd as m
+    m.load()
+    return m
+
+
+def _conv_problem(B, L, D, N, dtype, K, seed, bias=True, tok=False, **kw):
+    p = _problem(B, L, D, N, dtype, seed=seed, h0=True, **kw)
+    p["x"] = p.pop("u")
+    p["conv_w"], p["conv_b"] = conv_inputs(D, K, seed=seed, with_bias=bias)
+    if tok:
+        p["delta"] = p["delta"][:, :, 0].contiguous()
+    return p
+
+
+def _okw(p):
+    k = _oracle_kwargs(dict(p, u=p["x"]))
+    k.pop("u")
+    return dict(k, x=p["x"], conv_w=p["conv_w"], conv_b=p["conv_b"])
+
+
+def _gpu_fwd(ssm, p, zoh=False, **kw):
+    return ssm.scan_fwd_conv(p["x"], p["conv_w"], p["conv_b"], p["delta"], p["A"], p["B"], p["C"],
+                             p.get("D"), p.get("z"), p.get("delta_bias"),
+                             p.get("delta_softplus", True), p.get("h0"), zoh=zoh, **kw)
+
+
+@pytest.mark.parametrize("B,L,D,N,dtype,K", [
+    (2, 300, 72, 16, torch.float32, 4), (2, 300, 72, 16, torch.bfloat16, 4),
+    (3, 97, 136, 8, torch.float32, 3), (2, 45, 64, 1, torch.float32, 2),
+    (1, 70, 16, 2, torch.bfloat16, 1), (1, 3, 8, 4, torch.float32, 4)])
+@pytest.mark.parametrize("opts", [dict(), dict(zoh=True, tok=True, bias=False)], ids=["plain", "zoh-tok"])
+def test_fwd_conv_small(ssm, B, L, D, N, dtype, K, opts):
+    opts = dict(opts)  # the parametrised dict is shared between cases
+    zoh = opts.pop("zoh", False)
+    p = _conv_problem(B, L, D, N, dtype, K, seed=L + K, **opts)
+    T = ssm.chunk_len()
+    y, hf, cs = _gpu_fwd(ssm, _to(p, "cuda"), zoh, return_final_state=True, save_chunk_states=True)
+    torch.cuda.synchronize()
+    yo, hfo, cso = oracle_c.scan_fwd_conv(**_okw(p), chunk_len=T, zoh=zoh)
+    tol = TOL[dtype]
+    assert nmax_err(y, yo) <= tol
+    assert nmax_err(hf, hfo) <= tol
+    assert nmax_err(cs.permute(0, 1, 3, 2), cso) <= tol
+
+
+def test_fwd_conv_sequence_split(ssm):
+    p = _conv_problem(1, 10000, 16, 16, torch.float32, 4, seed=3)
+    y, hf, _ = _gpu_fwd(ssm, _to(p, "cuda"), return_final_state=True)
+    torch.cuda.synchronize()
+    yo, hfo, _ = oracle_c.scan_fwd_conv(**_okw(p))
+    assert nmax_err(y, yo) <= 1e-4 and nmax_err(hf, hfo) <= 1e-4
+
+
+def test_fwd_conv_workload1_full_size(ssm):
+    """The Mamba-370m shape with a width-4 convolution, on sampled channels
+    (the convolution is per channel, so the oracle runs on the slice)."""
+    w = WORKLOADS[1]
+    p = workload_inputs(1, device="cuda")
+    cw, cb = conv_inputs(w.dim, 4, seed=1, device="cuda")
+    y, hf, _ = ssm.scan_fwd_conv(p["u"], cw, cb, p["delta"], p["A"], p["B"], p["C"], p["D"],
+                                 p["z"], p["delta_bias"], True, None, return_final_state=True)
+    torch.cuda.synchronize()
+    sel = torch.randperm(w.dim, generator=torch.Generator().manual_seed(5))[:12].sort().values
+    sc = sel.cuda()
+    yo, hfo, _ = oracle_c.scan_fwd_conv(
+        p["u"][:, :, sc].cpu(), cw[sc].cpu(), cb[sc].cpu(), p["delta"][:, :, sc].cpu(),
+        p["A"][sc].cpu(), p["B"].cpu(), p["C"].cpu(), p["D"][sc].cpu(), p["z"][:, :, sc].cpu(),
+        p["delta_bias"][sc].cpu(), True)
+    assert nmax_err(y[:, :, sc], yo) <= 1e-4 and nmax_err(hf[:, sc], hfo) <= 1e-4
+
+
+def _check_bwd(ssm, p, tol, zoh=False, seed=0):
+    pg = _to(p, "cuda")
+    y, hf, cs = _gpu_fwd(ssm, pg, zoh, return_final_state=True, save_chunk_states=True)
+    dy = cotangent(y, seed)
+    dhf = torch.randn(hf.shape, generator=torch.Generator().manual_seed(seed)).cuda()
+    gr = ssm.scan_bwd_conv(pg["x"], pg["conv_w"], pg["conv_b"], pg["delta"], pg["A"], pg["B"],
+                           pg["C"], pg.get("D"), pg.get("z"), pg.get("delta_bias"), True,
+                           pg.get("h0"), cs, dy, dhf, zoh=zoh)
+    torch.cuda.synchronize()
+    go = oracle_c.scan_bwd_conv(**_okw(p), dy=dy.cpu(), dh_final=dhf.cpu(), zoh=zoh)
+    for k in GRADS:
+        if go.get(k) is None or gr.get(k) is None:
+            assert go.get(k) is None and gr.get(k) is None, k
+            continue
+        assert tuple(gr[k].shape) == go[k].shape, k
+        err = nmax_err(gr[k], go[k])
+        assert err <= tol, (k, err)
+
+
+@pytest.mark.parametrize("B,L,D,N,dtype,K", [
+    (2, 300, 72, 16, torch.float32, 4), (2, 300, 72, 16, torch.bfloat16, 4),
+    (3, 97, 136, 8, torch.float32, 3), (2, 45, 64, 1, torch.float32, 2),
+    (1, 600, 16, 2, torch.float32, 1)])
+@pytest.mark.parametrize("zoh", [False, True])
+def test_bwd_conv_small(ssm, B, L, D, N, dtype, K, zoh):
+    p = _conv_problem(B, L, D, N, dtype, K, seed=L + 3 * K)
+    _check_bwd(ssm, p, TOL[dtype], zoh=zoh, seed=K)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_bwd_conv_sequence_split_per_token(ssm, dtype):
+    p = _conv_problem(1, 5000, 16, 16, dtype, 4, seed=9, tok=True)
+    _check_bwd(ssm, p, TOL[dtype], seed=2)
+
+
+def test_conv_autograd(ssm):
+    p = _to(_conv_problem(2, 130, 64, 16, torch.float32, 4, seed=23), "cuda")
+    names = ("x", "conv_w", "conv_b", "delta", "A", "B", "C", "D", "z", "delta_bias", "h0")
+    leaves = {k: p[k].clone().requires_grad_(True) for k in names}
+    y, hf = ssm.conv_selective_scan(leaves["x"], leaves["conv_w"], leaves["conv_b"],
+                                    leaves["delta"], leaves["A"], leaves["B"], leaves["C"],
+                                    leaves["D"], leaves["z"], leaves["delta_bias"], True,
+                                    leaves["h0"])
+    dy = cotangent(y.detach(), 4)
+    (y * dy).sum().backward()
+    pc = {k: v.detach().cpu() for k, v in p.items() if isinstance(v, torch.Tensor)}
+    go = oracle_c.scan_bwd_conv(**_okw(dict(pc, delta_softplus=True)), dy=dy.cpu())
+    gname = dict(x="dx", conv_w="dconv_w", conv_b="dconv_b", delta="ddelta", A="dA", B="dB",
+                 C="dC", D="dD", z="dz", delta_bias="ddelta_bias", h0="dh0")
+    for k, g in gname.items():
+        assert nmax_err(leaves[k].grad, go[g]) <= 1e-4, k

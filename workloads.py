@@ -150,6 +150,16 @@ def decode_inputs(batch: int, dim: int, dstate: int, steps: int, io_dtype=torch.
                 C=Cm, D=Dskip, z=z, delta_bias=inverse_softplus(dt), delta_softplus=True)
 
 
+def conv_inputs(dim: int, width: int = 4, seed: int = 0, device="cpu", with_bias: bool = True):
+    """Taps (dim, width) ~ N(0, 0.5^2) and bias (dim) ~ N(0, 0.3^2), fp32, of the
+    causal depthwise convolution in front of the scan (drawn in that order from
+    their own generator, seed + 2,000,003)."""
+    g = _gen(seed + 2_000_003, device)
+    w = normal(g, (dim, width), torch.float32, device, std=0.5)
+    b = normal(g, (dim,), torch.float32, device, std=0.3)
+    return w, (b if with_bias else None)
+
+
 def workload_inputs(index: int, device="cpu", seed: Optional[int] = None):
     w = WORKLOADS[index]
     s = index if seed is None else seed

@@ -34,7 +34,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 WORKLOAD_NAMES = ["mamba-370m-layer-fwd", "mamba-2.8b-layer-fwd", "decode-state-update",
                   "million-length-fwd", "million-length-bwd", "mamba-370m-layer-bwd",
                   "mamba-370m-layer-fwd-zoh", "mamba-370m-layer-fwd-token-delta",
-                  "mamba-370m-layer-bidirectional", "decode-state-update-zoh"]
+                  "mamba-370m-layer-bidirectional", "decode-state-update-zoh",
+                  "mamba-370m-layer-fwd-conv4", "mamba-370m-layer-bwd-conv4"]
 METRIC = "selective-scan fwd tokens·channels/s and HBM GB/s (% of peak), Mamba-370m shape"
 UNIT = "tokens*channels/s"
 
@@ -153,7 +154,7 @@ def copy_calibration(nbytes=1 << 30, reps=5):
             "bytes_written_per_launch": nbytes, "launches": reps}
 
 
-def bench_fwd(args, idx, name, zoh=False, per_token=False, bidirectional=False):
+def bench_fwd(args, idx, name, zoh=False, per_token=False, bidirectional=False, conv=0):
     """Forward scan of workload ``idx``; options: the exact zero-order-hold
     input term, one step size per token (delta drawn as (B, L)), or both scan
     directions summed (two launches, the second accumulating into y)."""
@@ -166,10 +167,18 @@ def bench_fwd(args, idx, name, zoh=False, per_token=False, bidirectional=False):
     sets = [workload_inputs(idx, device="cuda", seed=idx + 100 * r) for r in range(args.rotate)]
     if per_token:  # one raw step size per token: the first channel's draw
         sets = [dict(p, delta=p["delta"][:, :, 0].contiguous()) for p in sets]
+    if conv:  # u is the convolution's input x; taps and bias of width ``conv``
+        from workloads import conv_inputs
+        for r, p in enumerate(sets):
+            p["conv_w"], p["conv_b"] = conv_inputs(w.dim, conv, seed=idx + 100 * r, device="cuda")
     torch.cuda.synchronize()
 
     def step(p):
-        if bidirectional:
+        if conv:
+            m.scan_fwd_conv(p["u"], p["conv_w"], p["conv_b"], p["delta"], p["A"], p["B"], p["C"],
+                            p["D"], p["z"], p["delta_bias"], True, None,
+                            return_final_state=want_hf, zoh=zoh)
+        elif bidirectional:
             m.bidirectional_scan(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
                                  p["delta_bias"], True, zoh=zoh)
         else:
@@ -182,6 +191,8 @@ def bench_fwd(args, idx, name, zoh=False, per_token=False, bidirectional=False):
     nbytes = algorithmic_bytes_fwd(Bsz, L, D, N, io_bytes, h_final=want_hf)
     if per_token:  # delta is (B, L) instead of (B, L, D)
         nbytes -= Bsz * L * (D - 1) * io_bytes
+    if conv:  # x replaces u; taps and bias are read once
+        nbytes += D * (conv + 1) * 4
     achieved = nbytes / (ms_launch * 1e-3) / 1e9
     sha = _source_sha("scan_fwd.hip", "device_common.hpp", "kernels.hpp")
     traffic = _traffic(f"fwd:{name}", sha)
@@ -199,10 +210,10 @@ def bench_fwd(args, idx, name, zoh=False, per_token=False, bidirectional=False):
                    "gpu": torch.cuda.get_device_name(), "wall_s": round(wall, 4),
                    "prewarm_steps": _time_launches.prewarm_steps,
                    "options": {"zoh": zoh, "delta_per_token": per_token,
-                               "bidirectional": bidirectional}},
+                               "bidirectional": bidirectional, "conv_width": conv}},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic if not (zoh or per_token or bidirectional) else None,
+                     "traffic": traffic if not (zoh or per_token or bidirectional or conv) else None,
                      "algorithmic_bytes": nbytes,
                      "kernel_ms": ms_launch, "source_sha": sha},
     }
@@ -247,23 +258,33 @@ def bench_decode(args, zoh=False):
                          "algorithmic_bytes": nbytes, "kernel_ms": ms_launch}}
 
 
-def bench_bwd(args, idx, name):
+def bench_bwd(args, idx, name, conv=0):
     """Backward of workload ``idx`` (one forward with chunk states runs first,
-    outside the timed steps)."""
+    outside the timed steps); ``conv``: with the fused convolution of that width."""
     import torch
 
     import selective_state_space_10_amd as m
     from workloads import WORKLOADS, cotangent, workload_inputs
     w = WORKLOADS[idx]
     p = workload_inputs(idx, device="cuda")
-    y, _, cs = m.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
-                          p["delta_bias"], True, None, save_chunk_states=True)
+    if conv:
+        from workloads import conv_inputs
+        cw, cb = conv_inputs(w.dim, conv, seed=idx, device="cuda")
+        y, _, cs = m.scan_fwd_conv(p["u"], cw, cb, p["delta"], p["A"], p["B"], p["C"], p["D"],
+                                   p["z"], p["delta_bias"], True, None, save_chunk_states=True)
+    else:
+        y, _, cs = m.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                              p["delta_bias"], True, None, save_chunk_states=True)
     dy = cotangent(y, idx)
     del y
 
     def step(_):
-        m.scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["delta_bias"],
-                   True, None, cs, dy)
+        if conv:
+            m.scan_bwd_conv(p["u"], cw, cb, p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                            p["delta_bias"], True, None, cs, dy)
+        else:
+            m.scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                       p["delta_bias"], True, None, cs, dy)
 
     ms_step, ms_launch, wall = _time_launches(step, args.steps, args.warmup, [0])
     Bsz, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
@@ -321,6 +342,10 @@ def main():
         line = bench_decode(args, zoh=True)
     elif wl == "mamba-370m-layer-bwd":
         line = bench_bwd(args, 1, wl)
+    elif wl == "mamba-370m-layer-fwd-conv4":
+        line = bench_fwd(args, 1, wl, conv=4)
+    elif wl == "mamba-370m-layer-bwd-conv4":
+        line = bench_bwd(args, 1, wl, conv=4)
     else:
         line = bench_bwd(args, 4, wl)
     print(json.dumps(line), flush=True)

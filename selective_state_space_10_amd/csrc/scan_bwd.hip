@@ -207,12 +207,21 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
     const float4 v = *(const float4 *)(a.bias + dgc);
     bias4[0] = v.x, bias4[1] = v.y, bias4[2] = v.z, bias4[3] = v.w;
   }
-  float cw[4][XK], cb4[4] = {0.f, 0.f, 0.f, 0.f};  // convolution taps and bias of the group
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-#pragma unroll
-    for (int kk = 0; kk < XK; ++kk) cw[q][kk] = kk < ck ? a.conv_w[(dgc + q) * ck + kk] : 0.0f;
-    if (ck && a.conv_b) cb4[q] = a.conv_b[dgc + q];
+  // convolution taps (zero past the width) and bias per channel, in LDS: read in
+  // the prologue only, so they hold no registers through the recurrence
+  __shared__ __attribute__((aligned(16))) float CWB[CONV ? CPW : 1][kMaxConv + 1];
+  if (CONV) {
+    for (int i = tid; i < CPW * (kMaxConv + 1); i += NT) {
+      const int c = i / (kMaxConv + 1), kk = i % (kMaxConv + 1);
+      const int64_t dd = d0 + c < D ? d0 + c : D - 1;
+      float v = 0.0f;
+      if (kk < ck)
+        v = a.conv_w[dd * ck + kk];
+      else if (kk == kMaxConv && a.conv_b)
+        v = a.conv_b[dd];
+      CWB[c][kk] = v;
+    }
+    __syncthreads();
   }
 
   // --- sweep ownership: channel d0 + lane, slot s holds state w*NPL + (s ^ par)
@@ -291,14 +300,15 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
       const float4 r4 = V::cvt(r_dl[j]), g4 = V::cvt(r_dy[j]);
       float4 x4 = make_float4(0.f, 0.f, 0.f, 0.f);
       if (MODE == 0 && CONV) {  // u = silu(pre), pre = bias + sum_k w_k x[t - (K-1) + k]; keep silu'(pre)
-        float pre[4] = {cb4[0], cb4[1], cb4[2], cb4[3]};
+        const int cg = 4 * g;
+        float pre[4] = {CWB[cg][kMaxConv], CWB[cg + 1][kMaxConv], CWB[cg + 2][kMaxConv], CWB[cg + 3][kMaxConv]};
 #pragma unroll
         for (int kk = 0; kk < XK; ++kk) {
           const float4 xv = V::cvt(r_x[j][kk]);
-          pre[0] = fmaf(cw[0][kk], xv.x, pre[0]);
-          pre[1] = fmaf(cw[1][kk], xv.y, pre[1]);
-          pre[2] = fmaf(cw[2][kk], xv.z, pre[2]);
-          pre[3] = fmaf(cw[3][kk], xv.w, pre[3]);
+          pre[0] = fmaf(CWB[cg][kk], xv.x, pre[0]);
+          pre[1] = fmaf(CWB[cg + 1][kk], xv.y, pre[1]);
+          pre[2] = fmaf(CWB[cg + 2][kk], xv.z, pre[2]);
+          pre[3] = fmaf(CWB[cg + 3][kk], xv.w, pre[3]);
         }
         float uv[4], sd[4];
 #pragma unroll

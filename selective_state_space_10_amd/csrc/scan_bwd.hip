@@ -66,7 +66,7 @@ struct BwdWs {
   int64_t ntiles, nseg, seg_len, nrb;
 };
 
-constexpr int64_t kConvRows = 256;  // rows per block of the convolution backward
+constexpr int64_t kConvRows = 64;  // rows per block of the convolution backward
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 

@@ -178,3 +178,18 @@ def test_python_binding_rejects_cpu_tensors():
     A = -torch.ones(8, 4)
     with pytest.raises(ValueError, match="GPU"):
         scan_fwd(x, x, A, torch.zeros(1, 4, 4), torch.zeros(1, 4, 4))
+
+
+def test_header_compiles_as_c_and_cpp(tmp_path):
+    """The C ABI header is plain C: it compiles with gcc as C11 and as C++."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    src = tmp_path / "use.c"
+    src.write_text('#include "ssm_scan.h"\nint main(void) { return SSM_OK + SSM_FLAG_ZOH - 1; }\n')
+    inc = os.path.dirname(HEADER)
+    for lang in (["-x", "c", "-std=c11"], ["-x", "c++", "-std=c++17"]):
+        r = subprocess.run(["gcc", *lang, "-Wall", "-Werror", "-fsyntax-only", "-I", inc, str(src)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr

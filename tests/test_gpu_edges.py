@@ -1,0 +1,85 @@
+"""Edge cases of the HIP path against the oracle: lengths around the chunk
+length, the smallest channel count, many short rows, NaN propagation, and
+inputs the binding must refuse."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle_c
+from tests.helpers import nmax_err
+from tests.test_gpu_parity import TOL, _check_bwd, _check_fwd, _gpu_fwd, _problem, _to
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_10_amd as m
+    m.load()
+    return m
+
+
+@pytest.mark.parametrize("L", [1, 2, 31, 32, 33, 63, 64, 65])
+def test_lengths_around_the_chunk(ssm, L):
+    """One chunk is 32 steps: lengths just below, at and above one and two chunks."""
+    p = _problem(2, L, 72, 16, torch.float32, seed=L, h0=True)
+    _check_fwd(ssm, p, 1e-4)
+    _check_bwd(ssm, p, 1e-4, seed=L)
+
+
+@pytest.mark.parametrize("B,L,D,N,dtype", [(1, 40, 8, 16, torch.float32),
+                                           (5, 33, 8, 4, torch.bfloat16),
+                                           (64, 7, 64, 16, torch.float32),
+                                           (3, 50, 200, 16, torch.bfloat16)])
+def test_small_channel_counts_and_short_rows(ssm, B, L, D, N, dtype):
+    """8 channels (one partially filled tile), many short rows, and a channel
+    count that leaves a 8-channel tail in the last 64-channel tile."""
+    p = _problem(B, L, D, N, dtype, seed=B + L + D, h0=True)
+    _check_fwd(ssm, p, TOL[dtype])
+    _check_bwd(ssm, p, TOL[dtype], seed=B)
+
+
+def test_nan_propagates_in_its_channel_only(ssm):
+    """A NaN input poisons its own channel from that step on (through the
+    state) and nothing else: channels are independent recurrences."""
+    p = _to(_problem(1, 100, 72, 16, torch.float32, seed=2), "cuda")
+    p["u"][0, 40, 5] = float("nan")
+    y, hf, _ = _gpu_fwd(ssm, p, return_final_state=True)
+    torch.cuda.synchronize()
+    yc = y[0].cpu()
+    assert torch.isfinite(yc[:40]).all()
+    assert torch.isnan(yc[40:, 5]).all()
+    others = torch.cat([yc[:, :5], yc[:, 6:]], dim=1)
+    assert torch.isfinite(others).all()
+    assert torch.isnan(hf[0, 5]).all() and torch.isfinite(torch.cat([hf[0, :5], hf[0, 6:]])).all()
+
+
+def test_decode_matches_scan_for_many_small_rows(ssm):
+    p = _to(_problem(32, 3, 8, 16, torch.float32, seed=6, h0=True), "cuda")
+    y, hf, _ = _gpu_fwd(ssm, p, return_final_state=True)
+    state = p["h0"].clone()
+    for t in range(3):
+        yt = ssm.state_update(state, p["u"][:, t].contiguous(), p["delta"][:, t].contiguous(),
+                              p["A"], p["B"][:, t].contiguous(), p["C"][:, t].contiguous(),
+                              p["D"], p["z"][:, t].contiguous(), p["delta_bias"], True)
+        assert nmax_err(yt, y[:, t]) <= 1e-5
+    assert nmax_err(state, hf) <= 1e-5
+
+
+def test_binding_refuses_bad_inputs(ssm):
+    p = _to(_problem(2, 40, 16, 4, torch.float32, seed=1), "cuda")
+    args = [p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["delta_bias"]]
+    with pytest.raises(ValueError, match="contiguous"):
+        ssm.scan_fwd(p["u"].transpose(1, 2).contiguous().transpose(1, 2), *args[1:])
+    with pytest.raises(TypeError, match="dtype"):
+        ssm.scan_fwd(args[0], args[1], args[2].double(), *args[3:])
+    with pytest.raises(ValueError, match="shape"):
+        ssm.scan_fwd(args[0], args[1], args[2][:8], *args[3:])
+    with pytest.raises(TypeError, match="io dtype"):
+        ssm.scan_fwd(args[0].half(), *args[1:])
+    with pytest.raises(ValueError, match="width"):
+        ssm.scan_fwd_conv(args[0], torch.zeros(16, 5, device="cuda"), None, *args[1:5])

@@ -340,6 +340,272 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
   }
 }
 
+// Returns z (always 0) through an opaque register move that reads every 32-bit
+// word of the given values: code whose operands depend on the result cannot be
+// scheduled before those values are computed and read.
+template <typename... Ts>
+__device__ __forceinline__ int after_all(int z, const Ts &...vals) {
+  constexpr int W = (0 + ... + (int)(sizeof(Ts) / 4));
+  uint32_t w[W];
+  int n = 0;
+  auto put = [&](const auto &v) {
+    static_assert(sizeof(v) % 4 == 0, "whole 32-bit words");
+    const auto *p = reinterpret_cast<const uint32_t *>(&v);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(v) / 4); ++i) w[n++] = p[i];
+  };
+  (put(vals), ...);
+#pragma unroll
+  for (int i = 0; i < W; i += 8) {  // eight words per move
+    auto at = [&](int k) { return w[i + k < W ? i + k : W - 1]; };
+    int out;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(out)
+                 : "v"(z), "v"(at(0)), "v"(at(1)), "v"(at(2)), "v"(at(3)), "v"(at(4)), "v"(at(5)),
+                   "v"(at(6)), "v"(at(7))
+                 : "memory");
+    z = out;
+  }
+  return z;
+}
+
+// Forward with wave specialisation: 16 states, 64-channel tiles, no options,
+// no sequence split.  NRW recurrence waves only run the recurrence, 16 / NRW
+// states per lane (lane = channel).  Four service waves do everything else
+// for the same tile: global loads a few sub-chunks ahead, the step-size
+// prologue and B/C staging of the next sub-chunk, and the epilogue (sum of
+// the NRW partials, D*u, gate, store) of the previous one.  A sub-chunk is
+// T steps; LDS buffers alternate between sub-chunks, so one barrier per
+// sub-chunk orders everything.  On gfx950 plain arithmetic from one wave
+// fills issue slots that a recurrence wave on the same SIMD leaves free.
+template <typename IO, int NRW, int T, int R>
+__global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
+  constexpr int N = 16, CPW = 64, SPL = N / NRW;
+  constexpr int G = CPW / 4;        // 4-channel groups
+  constexpr int NV = 256;           // service threads
+  constexpr int IPT = T * G / NV;   // (step, channel group) items per service thread
+  constexpr int BPT = T * N / NV;   // B and C values per service thread
+  static_assert(SPL * NRW == N && SPL % 2 == 0, "states split evenly, B/C in float4 pieces");
+  static_assert(IPT >= 1 && BPT >= 1 && kChunkLen % T == 0, "sub-chunks tile the chunk");
+  using V = Vec4<IO>;
+  typedef typename V::raw raw_t;
+
+  const IO *__restrict__ u = (const IO *)a.u;
+  const IO *__restrict__ dl = (const IO *)a.delta;
+  const IO *__restrict__ zz = (const IO *)a.z;
+  const IO *__restrict__ Bm = (const IO *)a.Bm;
+  const IO *__restrict__ Cm = (const IO *)a.Cm;
+  IO *__restrict__ y = (IO *)a.y;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t L = a.L, D = a.D;
+  const int64_t b = blockIdx.y;
+  const int64_t d0 = (int64_t)blockIdx.x * CPW;
+  const int64_t row0 = b * L;
+  const int64_t nck = (L + T - 1) / T;  // sub-chunks
+  const int64_t K = (L + kChunkLen - 1) / kChunkLen;
+
+  __shared__ __attribute__((aligned(16))) float2 P[2][T][CPW];            // (dt, dt*u)
+  __shared__ __attribute__((aligned(16))) float BC[2][T][NRW][2 * SPL];  // B then C per recurrence wave
+  __shared__ __attribute__((aligned(16))) float Y[2][T][NRW][64];        // per-lane partial sums
+
+  if (w < NRW) {  // ------------------------------------------- recurrence waves
+    const int64_t d = d0 + lane;
+    const bool dv = d < D;
+    const int64_t dc = dv ? d : D - 1;
+    float Ap[SPL], h[SPL];
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) {
+      const int n = w * SPL + k;
+      Ap[k] = a.A[dc * N + n] * kLog2e;
+      h[k] = a.h0 ? a.h0[(b * D + dc) * N + n] : 0.0f;
+    }
+    __syncthreads();  // sub-chunk 0 staged
+    for (int64_t k = 0; k < nck; ++k) {
+      const int buf = (int)(k & 1);
+      if (a.chunk_states && dv && (k * T) % kChunkLen == 0) {
+        float *cs = a.chunk_states + ((b * K + k * T / kChunkLen) * N + w * SPL) * D + d;
+#pragma unroll
+        for (int kk = 0; kk < SPL; ++kk) cs[kk * D] = h[kk];
+      }
+#pragma unroll
+      for (int tl = 0; tl < T; ++tl) {
+        const float2 p = P[buf][tl][lane];
+        float bc[2 * SPL];
+#pragma unroll
+        for (int i = 0; i < SPL / 2; ++i) {
+          const float4 q = *(const float4 *)&BC[buf][tl][w][4 * i];
+          bc[4 * i] = q.x, bc[4 * i + 1] = q.y, bc[4 * i + 2] = q.z, bc[4 * i + 3] = q.w;
+        }
+        float ys = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < SPL; ++kk) {
+          const float da = fast_exp2(p.x * Ap[kk]);
+          h[kk] = fmaf(da, h[kk], p.y * bc[kk]);
+          ys = fmaf(bc[SPL + kk], h[kk], ys);
+        }
+        Y[buf][tl][w][lane] = ys;
+      }
+      __syncthreads();
+    }
+    if (a.h_final && dv) {
+#pragma unroll
+      for (int kk = 0; kk < SPL; ++kk) a.h_final[(b * D + d) * N + w * SPL + kk] = h[kk];
+    }
+    return;  // the service waves' last epilogue needs no further barrier
+  }
+
+  // ---------------------------------------------------------------- service waves
+  const int vt = tid - NRW * 64;
+  const int g = vt % G;
+  const int tl0 = vt / G;  // items: steps tl0 + j * (NV / G)
+  const int64_t dg = d0 + 4 * g;
+  const bool gv = dg < D;  // D % 4 == 0: a group is all valid or all not
+  const int64_t dgc = gv ? dg : D - 4;
+  const bool has_z = a.z != nullptr;
+  const IO *__restrict__ zsrc = has_z ? zz : u;  // loaded either way, so no register slot is conditional
+  const bool sp = a.softplus != 0;
+  float bias4[4] = {0.f, 0.f, 0.f, 0.f}, Dsk4[4] = {0.f, 0.f, 0.f, 0.f};
+  if (a.bias) {
+    const float4 v = *(const float4 *)(a.bias + dgc);
+    bias4[0] = v.x, bias4[1] = v.y, bias4[2] = v.z, bias4[3] = v.w;
+  }
+  if (a.Dskip) {
+    const float4 v = *(const float4 *)(a.Dskip + dgc);
+    Dsk4[0] = v.x, Dsk4[1] = v.y, Dsk4[2] = v.z, Dsk4[3] = v.w;
+  }
+
+  raw_t r_dl[R][IPT], r_u[R][IPT], r_z[R][IPT];  // loads in flight: sub-chunk j in slot j % R
+  float r_b[R][BPT], r_c[R][BPT];
+  float4 keep_du[2][IPT], keep_g[2][IPT];         // D*u and silu(z), by sub-chunk parity
+
+  auto load_chunk = [&](int64_t k, raw_t(&ra)[IPT], raw_t(&ru)[IPT], raw_t(&rz)[IPT], float(&rb)[BPT],
+                        float(&rc)[BPT]) {
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int64_t t = k * T + tl0 + j * (NV / G);
+      const int64_t idx = (row0 + (t < L ? t : L - 1)) * D + dgc;
+      ra[j] = V::load(dl, idx);
+      ru[j] = V::load(u, idx);
+      rz[j] = V::load(zsrc, idx);
+    }
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int i = vt + j * NV;
+      const int64_t t = k * T + i / N;
+      const int64_t idx = (row0 + (t < L ? t : L - 1)) * N + i % N;
+      rb[j] = load_io(Bm, idx);
+      rc[j] = load_io(Cm, idx);
+    }
+  };
+  auto prologue = [&](int64_t k, raw_t(&ra)[IPT], raw_t(&ru)[IPT], raw_t(&rz)[IPT], float(&rb)[BPT],
+                      float(&rc)[BPT], float4(&kdu)[IPT], float4(&kg)[IPT]) {
+    const int buf = (int)(k & 1);
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int tl = tl0 + j * (NV / G);
+      const bool tv = k * T + tl < L;  // steps past the end get dt = 0: no state change
+      const float4 r = V::cvt(ra[j]), x = V::cvt(ru[j]);
+      const float rv[4] = {r.x, r.y, r.z, r.w}, xv[4] = {x.x, x.y, x.z, x.w};
+      float dt[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float s = rv[q] + bias4[q];
+        const float sv = softplus_f(s);
+        dt[q] = tv ? (sp ? sv : s) : 0.0f;
+      }
+      float4 *pp = (float4 *)&P[buf][tl][4 * g];
+      pp[0] = make_float4(dt[0], dt[0] * xv[0], dt[1], dt[1] * xv[1]);
+      pp[1] = make_float4(dt[2], dt[2] * xv[2], dt[3], dt[3] * xv[3]);
+      // D*u now rather than in the epilogue: a product, unlike u itself, is a
+      // new value, so the raw slot can be refilled without a register copy
+      // that would wait for the refill's loads.
+      kdu[j] = make_float4(Dsk4[0] * x.x, Dsk4[1] * x.y, Dsk4[2] * x.z, Dsk4[3] * x.w);
+      if (has_z) {
+        const float4 zv = V::cvt(rz[j]);
+        kg[j] = make_float4(silu_f(zv.x), silu_f(zv.y), silu_f(zv.z), silu_f(zv.w));
+      } else {
+        kg[j] = make_float4(1.f, 1.f, 1.f, 1.f);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int i = vt + j * NV;
+      const int tl = i / N, n = i % N;
+      BC[buf][tl][n / SPL][n % SPL] = rb[j];
+      BC[buf][tl][n / SPL][SPL + n % SPL] = rc[j];
+    }
+  };
+  auto epilogue = [&](int64_t k, const float4(&kdu)[IPT], const float4(&kg)[IPT]) {
+    const int buf = (int)(k & 1);
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int tl = tl0 + j * (NV / G);
+      const int64_t t = k * T + tl;
+      if (t < L && gv) {
+        float4 s = *(const float4 *)&Y[buf][tl][0][4 * g];
+#pragma unroll
+        for (int ww = 1; ww < NRW; ++ww) {
+          const float4 v = *(const float4 *)&Y[buf][tl][ww][4 * g];
+          s.x += v.x, s.y += v.y, s.z += v.z, s.w += v.w;
+        }
+        s.x = (s.x + kdu[j].x) * kg[j].x;
+        s.y = (s.y + kdu[j].y) * kg[j].y;
+        s.z = (s.z + kdu[j].z) * kg[j].z;
+        s.w = (s.w + kdu[j].w) * kg[j].w;
+        V::store(y, (row0 + t) * D + dg, s);
+      }
+    }
+  };
+
+  // Loads and prologues of sub-chunks past the end are harmless (rows are
+  // clamped, steps past L get dt = 0, and nothing reads them), so they run
+  // unconditionally: a register slot that is only sometimes refilled would
+  // make the compiler copy it and wait for loads still in flight.
+#pragma unroll
+  for (int j = 0; j < R; ++j) load_chunk(j, r_dl[j], r_u[j], r_z[j], r_b[j], r_c[j]);
+  prologue(0, r_dl[0], r_u[0], r_z[0], r_b[0], r_c[0], keep_du[0], keep_g[0]);
+  load_chunk(R, r_dl[0], r_u[0], r_z[0], r_b[0], r_c[0]);
+  __syncthreads();  // sub-chunk 0 staged
+  // Iteration k (the recurrence waves scan sub-chunk k): epilogue of k-1,
+  // then prologue of k+1 and the loads of k+1+R into the slot it frees.
+  // The loop is unrolled so that every slot index is a constant.
+  constexpr int U = R % 2 ? 2 * R : R;
+  auto iteration = [&](int64_t k, const int i) {  // i = k % U
+    const int rs = (i + 1) % R, ks = (i + 1) % 2;  // slots of sub-chunk k+1 (and k-1 for ks)
+    if (k >= 1) epilogue(k - 1, keep_du[ks], keep_g[ks]);
+    prologue(k + 1, r_dl[rs], r_u[rs], r_z[rs], r_b[rs], r_c[rs], keep_du[ks], keep_g[ks]);
+    // The refill must follow the slot's last use: hoisted above it, it would
+    // need other registers and a copy at the loop edge that waits for it.
+    // The zero below is produced only after every value of the slot and every
+    // product of the prologue (so none of them is computed later from the
+    // slot), and the refill's addresses depend on it.
+    const int zero = after_all(after_all(0, keep_du[ks], keep_g[ks]), r_dl[rs], r_u[rs], r_z[rs], r_b[rs],
+                               r_c[rs]);
+    load_chunk(k + 1 + R + zero, r_dl[rs], r_u[rs], r_z[rs], r_b[rs], r_c[rs]);
+    __syncthreads();
+  };
+  int64_t k = 0;
+  for (; k + U <= nck; k += U) {
+#pragma unroll
+    for (int i = 0; i < U; ++i) iteration(k + i, i);
+  }
+#pragma unroll
+  for (int i = 0; i < U - 1; ++i)
+    if (k + i < nck) iteration(k + i, i);
+  if ((nck - 1) & 1)
+    epilogue(nck - 1, keep_du[1], keep_g[1]);
+  else
+    epilogue(nck - 1, keep_du[0], keep_g[0]);
+}
+
+// Wave-specialised forward configuration.  Measured on MI355X at 8 x 2048 x
+// 2048 x 16 (fp32): eight recurrence waves (two per SIMD, 2 states per lane)
+// with 16-step sub-chunks beat four (one per SIMD) with 32-step ones, and a
+// ring of two register slots beats four (which spills).
+constexpr int kWsRecWaves = 8, kWsSteps = 16, kWsRing = 2;
+
 // Second phase of a sequence split: the state entering every segment,
 // h_in[0] = h0, h_in[s+1] = exp(A * sum of dt over s) * h_in[s] + h_loc[s]
 // (composition of the affine maps h -> a h + b of consecutive segments).
@@ -417,6 +683,11 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   a.seg_len = split_len(a.B, a.L, a.D);
   const unsigned tiles = (unsigned)((a.D + CPW - 1) / CPW);
   if (a.seg_len == 0) {
+    if constexpr (N == 16 && CPW == 64 && !ZOH && !FLAGS) {
+      hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing>), dim3(tiles, (unsigned)a.B, 1),
+                         dim3(64 * (kWsRecWaves + 4)), 0, s, a);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0, ZOH, FLAGS>), dim3(tiles, (unsigned)a.B, 1), dim3(64 * NW), 0, s,
                        a);
     return hipGetLastError();

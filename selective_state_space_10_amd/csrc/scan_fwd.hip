@@ -368,8 +368,9 @@ __device__ __forceinline__ int after_all(int z, const Ts &...vals) {
   return z;
 }
 
-// Forward with wave specialisation: 16 states, 64-channel tiles, no options,
-// no sequence split.  NRW recurrence waves only run the recurrence, 16 / NRW
+// Forward with wave specialisation: 16 states, 64-channel tiles, no sequence
+// split; with FLAGS also the reverse direction, one step size per token and
+// accumulation into y (not the exact hold or the fused convolution).  NRW recurrence waves only run the recurrence, 16 / NRW
 // states per lane (lane = channel).  Four service waves do everything else
 // for the same tile: global loads a few sub-chunks ahead, the step-size
 // prologue and B/C staging of the next sub-chunk, and the epilogue (sum of
@@ -377,7 +378,7 @@ __device__ __forceinline__ int after_all(int z, const Ts &...vals) {
 // T steps; LDS buffers alternate between sub-chunks, so one barrier per
 // sub-chunk orders everything.  On gfx950 plain arithmetic from one wave
 // fills issue slots that a recurrence wave on the same SIMD leaves free.
-template <typename IO, int NRW, int T, int R>
+template <typename IO, int NRW, int T, int R, bool FLAGS>
 __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
   constexpr int N = 16, CPW = 64, SPL = N / NRW;
   constexpr int G = CPW / 4;        // 4-channel groups
@@ -466,6 +467,10 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
   const bool has_z = a.z != nullptr;
   const IO *__restrict__ zsrc = has_z ? zz : u;  // loaded either way, so no register slot is conditional
   const bool sp = a.softplus != 0;
+  const bool rev = FLAGS && (a.flags & kFlagReverse) != 0;
+  const bool tok = FLAGS && (a.flags & kFlagDeltaPerToken) != 0;
+  const bool accum = FLAGS && (a.flags & kFlagAccumulate) != 0;
+  auto mrow = [&](int64_t t) { return row0 + (rev ? L - 1 - t : t); };  // memory row of scan step t
   float bias4[4] = {0.f, 0.f, 0.f, 0.f}, Dsk4[4] = {0.f, 0.f, 0.f, 0.f};
   if (a.bias) {
     const float4 v = *(const float4 *)(a.bias + dgc);
@@ -485,8 +490,9 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int64_t t = k * T + tl0 + j * (NV / G);
-      const int64_t idx = (row0 + (t < L ? t : L - 1)) * D + dgc;
-      ra[j] = V::load(dl, idx);
+      const int64_t r = mrow(t < L ? t : L - 1);
+      const int64_t idx = r * D + dgc;
+      ra[j] = tok ? V::splat(dl, r) : V::load(dl, idx);
       ru[j] = V::load(u, idx);
       rz[j] = V::load(zsrc, idx);
     }
@@ -494,7 +500,7 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
     for (int j = 0; j < BPT; ++j) {
       const int i = vt + j * NV;
       const int64_t t = k * T + i / N;
-      const int64_t idx = (row0 + (t < L ? t : L - 1)) * N + i % N;
+      const int64_t idx = mrow(t < L ? t : L - 1) * N + i % N;
       rb[j] = load_io(Bm, idx);
       rc[j] = load_io(Cm, idx);
     }
@@ -554,7 +560,12 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
         s.y = (s.y + kdu[j].y) * kg[j].y;
         s.z = (s.z + kdu[j].z) * kg[j].z;
         s.w = (s.w + kdu[j].w) * kg[j].w;
-        V::store(y, (row0 + t) * D + dg, s);
+        const int64_t yi = mrow(t) * D + dg;
+        if (accum) {
+          const float4 o = V::cvt(V::load(y, yi));
+          s.x += o.x, s.y += o.y, s.z += o.z, s.w += o.w;
+        }
+        V::store(y, yi, s);
       }
     }
   };
@@ -683,11 +694,6 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   a.seg_len = split_len(a.B, a.L, a.D);
   const unsigned tiles = (unsigned)((a.D + CPW - 1) / CPW);
   if (a.seg_len == 0) {
-    if constexpr (N == 16 && CPW == 64 && !ZOH && !FLAGS) {
-      hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing>), dim3(tiles, (unsigned)a.B, 1),
-                         dim3(64 * (kWsRecWaves + 4)), 0, s, a);
-      return hipGetLastError();
-    }
     hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0, ZOH, FLAGS>), dim3(tiles, (unsigned)a.B, 1), dim3(64 * NW), 0, s,
                        a);
     return hipGetLastError();
@@ -716,6 +722,20 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
   constexpr int mincpw = 64 * NPL / N > 16 ? 64 * NPL / N : 16;
   // options use one tile width (fewer instantiations); the plain scan picks its own
   constexpr int OCPW = mincpw > 32 ? 64 : 32;
+  if constexpr (N == 16) {
+    // 64-channel tiles in one round over the CUs and no sequence split: the
+    // wave-specialised kernel, also for the options it implements
+    if (!(a.flags & kFlagZoh) && a.conv_k == 0 && pick_cpw<N>(a) == 64 && split_len(a.B, a.L, a.D) == 0) {
+      const unsigned tiles = (unsigned)((a.D + 63) / 64);
+      if (a.flags)
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true>), dim3(tiles, (unsigned)a.B, 1),
+                           dim3(64 * (kWsRecWaves + 4)), 0, s, a);
+      else
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false>), dim3(tiles, (unsigned)a.B, 1),
+                           dim3(64 * (kWsRecWaves + 4)), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if (a.flags & kFlagZoh) return launch_fwd_cpw<IO, N, OCPW, true, true>(a, s);
   if (a.flags || a.conv_k) return launch_fwd_cpw<IO, N, OCPW, false, true>(a, s);
   const int cpw = pick_cpw<N>(a);

@@ -404,7 +404,13 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
   const int64_t b = blockIdx.y;
   const int64_t d0 = (int64_t)blockIdx.x * CPW;
   const int64_t row0 = b * L;
-  const int64_t nck = (L + T - 1) / T;  // sub-chunks
+  // With a sequence split, workgroup z scans segment z from its composed
+  // start state; steps are counted from the segment's first step tb.
+  const int64_t seg = blockIdx.z;
+  const int64_t nseg = a.seg_len ? (L + a.seg_len - 1) / a.seg_len : 1;
+  const int64_t tb = a.seg_len ? seg * a.seg_len : 0;
+  const int64_t Ls = (a.seg_len && tb + a.seg_len < L ? tb + a.seg_len : L) - tb;  // steps in the segment
+  const int64_t nck = (Ls + T - 1) / T;  // sub-chunks
   const int64_t K = (L + kChunkLen - 1) / kChunkLen;
 
   __shared__ __attribute__((aligned(16))) float2 P[2][T][CPW];            // (dt, dt*u)
@@ -420,13 +426,16 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
     for (int k = 0; k < SPL; ++k) {
       const int n = w * SPL + k;
       Ap[k] = a.A[dc * N + n] * kLog2e;
-      h[k] = a.h0 ? a.h0[(b * D + dc) * N + n] : 0.0f;
+      if (a.seg_len)
+        h[k] = a.seg_state[((b * nseg + seg) * D + dc) * N + n];
+      else
+        h[k] = a.h0 ? a.h0[(b * D + dc) * N + n] : 0.0f;
     }
     __syncthreads();  // sub-chunk 0 staged
     for (int64_t k = 0; k < nck; ++k) {
       const int buf = (int)(k & 1);
-      if (a.chunk_states && dv && (k * T) % kChunkLen == 0) {
-        float *cs = a.chunk_states + ((b * K + k * T / kChunkLen) * N + w * SPL) * D + d;
+      if (a.chunk_states && dv && (k * T) % kChunkLen == 0) {  // tb is a multiple of kChunkLen
+        float *cs = a.chunk_states + ((b * K + (tb + k * T) / kChunkLen) * N + w * SPL) * D + d;
 #pragma unroll
         for (int kk = 0; kk < SPL; ++kk) cs[kk * D] = h[kk];
       }
@@ -450,7 +459,7 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
       }
       __syncthreads();
     }
-    if (a.h_final && dv) {
+    if (a.h_final && dv && tb + Ls == L) {
 #pragma unroll
       for (int kk = 0; kk < SPL; ++kk) a.h_final[(b * D + d) * N + w * SPL + kk] = h[kk];
     }
@@ -470,7 +479,9 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
   const bool rev = FLAGS && (a.flags & kFlagReverse) != 0;
   const bool tok = FLAGS && (a.flags & kFlagDeltaPerToken) != 0;
   const bool accum = FLAGS && (a.flags & kFlagAccumulate) != 0;
-  auto mrow = [&](int64_t t) { return row0 + (rev ? L - 1 - t : t); };  // memory row of scan step t
+  auto mrow = [&](int64_t t) {  // memory row of segment step t
+    return row0 + (rev ? L - 1 - (tb + t) : tb + t);
+  };
   float bias4[4] = {0.f, 0.f, 0.f, 0.f}, Dsk4[4] = {0.f, 0.f, 0.f, 0.f};
   if (a.bias) {
     const float4 v = *(const float4 *)(a.bias + dgc);
@@ -490,7 +501,7 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int64_t t = k * T + tl0 + j * (NV / G);
-      const int64_t r = mrow(t < L ? t : L - 1);
+      const int64_t r = mrow(t < Ls ? t : Ls - 1);
       const int64_t idx = r * D + dgc;
       ra[j] = tok ? V::splat(dl, r) : V::load(dl, idx);
       ru[j] = V::load(u, idx);
@@ -500,7 +511,7 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
     for (int j = 0; j < BPT; ++j) {
       const int i = vt + j * NV;
       const int64_t t = k * T + i / N;
-      const int64_t idx = mrow(t < L ? t : L - 1) * N + i % N;
+      const int64_t idx = mrow(t < Ls ? t : Ls - 1) * N + i % N;
       rb[j] = load_io(Bm, idx);
       rc[j] = load_io(Cm, idx);
     }
@@ -511,7 +522,7 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int tl = tl0 + j * (NV / G);
-      const bool tv = k * T + tl < L;  // steps past the end get dt = 0: no state change
+      const bool tv = k * T + tl < Ls;  // steps past the end get dt = 0: no state change
       const float4 r = V::cvt(ra[j]), x = V::cvt(ru[j]);
       const float rv[4] = {r.x, r.y, r.z, r.w}, xv[4] = {x.x, x.y, x.z, x.w};
       float dt[4];
@@ -549,7 +560,7 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
     for (int j = 0; j < IPT; ++j) {
       const int tl = tl0 + j * (NV / G);
       const int64_t t = k * T + tl;
-      if (t < L && gv) {
+      if (t < Ls && gv) {
         float4 s = *(const float4 *)&Y[buf][tl][0][4 * g];
 #pragma unroll
         for (int ww = 1; ww < NRW; ++ww) {
@@ -711,6 +722,18 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   hipLaunchKernelGGL(fwd_seg_combine_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, a, nseg);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if constexpr (N == 16 && !ZOH) {
+    if (a.conv_k == 0) {  // the segments' full scans: the wave-specialised kernel, 64-channel tiles
+      const dim3 grid((unsigned)((a.D + 63) / 64), (unsigned)a.B, (unsigned)nseg);
+      if (a.flags)
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true>), grid,
+                           dim3(64 * (kWsRecWaves + 4)), 0, s, a);
+      else
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false>), grid,
+                           dim3(64 * (kWsRecWaves + 4)), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0, ZOH, FLAGS>), dim3(tiles, (unsigned)a.B, (unsigned)nseg),
                      dim3(64 * NW), 0, s, a);
   return hipGetLastError();

@@ -60,11 +60,16 @@ def test_fwd_options_small(ssm, opts, B, L, D, N, dtype):
     _check_fwd(ssm, p, TOL[dtype], opts.get("zoh", False), opts.get("reverse", False))
 
 
+@pytest.mark.parametrize("zoh", [True, False], ids=["zoh", "no-zoh"])
 @pytest.mark.parametrize("B,L,D,N,dtype", [(1, 10000, 16, 16, torch.float32),
-                                           (2, 9000, 24, 8, torch.bfloat16)])
-def test_fwd_options_sequence_split(ssm, B, L, D, N, dtype):
+                                           (2, 9000, 24, 8, torch.bfloat16),
+                                           (1, 9001, 72, 16, torch.bfloat16)])
+def test_fwd_options_sequence_split(ssm, B, L, D, N, dtype, zoh):
+    """Reverse direction and one step size per token over a split sequence
+    (16 states without the exact hold: segments scanned by the wave-specialised
+    kernel)."""
     p = _with_opts(_problem(B, L, D, N, dtype, seed=7, h0=True), True)
-    _check_fwd(ssm, p, TOL[dtype], zoh=True, reverse=True)
+    _check_fwd(ssm, p, TOL[dtype], zoh=zoh, reverse=True)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])

@@ -370,7 +370,9 @@ __device__ __forceinline__ int after_all(int z, const Ts &...vals) {
 
 // Forward with wave specialisation: 16 states, 64-channel tiles, no sequence
 // split; with FLAGS also the reverse direction, one step size per token and
-// accumulation into y (not the exact hold or the fused convolution).  NRW recurrence waves only run the recurrence, 16 / NRW
+// accumulation into y (not the exact hold or the fused convolution).  MODE 1
+// is the first pass of a sequence split: each segment's end state from a zero
+// start and its sum of step sizes, no output.  NRW recurrence waves only run the recurrence, 16 / NRW
 // states per lane (lane = channel).  Four service waves do everything else
 // for the same tile: global loads a few sub-chunks ahead, the step-size
 // prologue and B/C staging of the next sub-chunk, and the epilogue (sum of
@@ -378,7 +380,7 @@ __device__ __forceinline__ int after_all(int z, const Ts &...vals) {
 // T steps; LDS buffers alternate between sub-chunks, so one barrier per
 // sub-chunk orders everything.  On gfx950 plain arithmetic from one wave
 // fills issue slots that a recurrence wave on the same SIMD leaves free.
-template <typename IO, int NRW, int T, int R, bool FLAGS>
+template <typename IO, int NRW, int T, int R, bool FLAGS, int MODE>
 __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
   constexpr int N = 16, CPW = 64, SPL = N / NRW;
   constexpr int G = CPW / 4;        // 4-channel groups
@@ -421,12 +423,14 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
     const int64_t d = d0 + lane;
     const bool dv = d < D;
     const int64_t dc = dv ? d : D - 1;
-    float Ap[SPL], h[SPL];
+    float Ap[SPL], h[SPL], dsum = 0.0f;
 #pragma unroll
     for (int k = 0; k < SPL; ++k) {
       const int n = w * SPL + k;
       Ap[k] = a.A[dc * N + n] * kLog2e;
-      if (a.seg_len)
+      if (MODE == 1)
+        h[k] = 0.0f;
+      else if (a.seg_len)
         h[k] = a.seg_state[((b * nseg + seg) * D + dc) * N + n];
       else
         h[k] = a.h0 ? a.h0[(b * D + dc) * N + n] : 0.0f;
@@ -434,7 +438,7 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
     __syncthreads();  // sub-chunk 0 staged
     for (int64_t k = 0; k < nck; ++k) {
       const int buf = (int)(k & 1);
-      if (a.chunk_states && dv && (k * T) % kChunkLen == 0) {  // tb is a multiple of kChunkLen
+      if (MODE == 0 && a.chunk_states && dv && (k * T) % kChunkLen == 0) {  // tb is a multiple of kChunkLen
         float *cs = a.chunk_states + ((b * K + (tb + k * T) / kChunkLen) * N + w * SPL) * D + d;
 #pragma unroll
         for (int kk = 0; kk < SPL; ++kk) cs[kk * D] = h[kk];
@@ -453,13 +457,22 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
         for (int kk = 0; kk < SPL; ++kk) {
           const float da = fast_exp2(p.x * Ap[kk]);
           h[kk] = fmaf(da, h[kk], p.y * bc[kk]);
-          ys = fmaf(bc[SPL + kk], h[kk], ys);
+          if (MODE == 0) ys = fmaf(bc[SPL + kk], h[kk], ys);
         }
-        Y[buf][tl][w][lane] = ys;
+        if (MODE == 0)
+          Y[buf][tl][w][lane] = ys;
+        else
+          dsum += p.x;
       }
       __syncthreads();
     }
-    if (a.h_final && dv && tb + Ls == L) {
+    if (MODE == 1) {
+      if (dv) {
+#pragma unroll
+        for (int kk = 0; kk < SPL; ++kk) a.seg_hloc[((b * nseg + seg) * D + d) * N + w * SPL + kk] = h[kk];
+        if (w == 0) a.seg_dsum[(b * nseg + seg) * D + d] = dsum;
+      }
+    } else if (a.h_final && dv && tb + Ls == L) {
 #pragma unroll
       for (int kk = 0; kk < SPL; ++kk) a.h_final[(b * D + d) * N + w * SPL + kk] = h[kk];
     }
@@ -505,7 +518,7 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
       const int64_t idx = r * D + dgc;
       ra[j] = tok ? V::splat(dl, r) : V::load(dl, idx);
       ru[j] = V::load(u, idx);
-      rz[j] = V::load(zsrc, idx);
+      if (MODE == 0) rz[j] = V::load(zsrc, idx);
     }
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
@@ -513,7 +526,7 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
       const int64_t t = k * T + i / N;
       const int64_t idx = mrow(t < Ls ? t : Ls - 1) * N + i % N;
       rb[j] = load_io(Bm, idx);
-      rc[j] = load_io(Cm, idx);
+      if (MODE == 0) rc[j] = load_io(Cm, idx);
     }
   };
   auto prologue = [&](int64_t k, raw_t(&ra)[IPT], raw_t(&ru)[IPT], raw_t(&rz)[IPT], float(&rb)[BPT],
@@ -538,6 +551,7 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
       // D*u now rather than in the epilogue: a product, unlike u itself, is a
       // new value, so the raw slot can be refilled without a register copy
       // that would wait for the refill's loads.
+      if (MODE == 1) continue;
       kdu[j] = make_float4(Dsk4[0] * x.x, Dsk4[1] * x.y, Dsk4[2] * x.z, Dsk4[3] * x.w);
       if (has_z) {
         const float4 zv = V::cvt(rz[j]);
@@ -551,7 +565,7 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
       const int i = vt + j * NV;
       const int tl = i / N, n = i % N;
       BC[buf][tl][n / SPL][n % SPL] = rb[j];
-      BC[buf][tl][n / SPL][SPL + n % SPL] = rc[j];
+      if (MODE == 0) BC[buf][tl][n / SPL][SPL + n % SPL] = rc[j];
     }
   };
   auto epilogue = [&](int64_t k, const float4(&kdu)[IPT], const float4(&kg)[IPT]) {
@@ -596,15 +610,18 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
   constexpr int U = R % 2 ? 2 * R : R;
   auto iteration = [&](int64_t k, const int i) {  // i = k % U
     const int rs = (i + 1) % R, ks = (i + 1) % 2;  // slots of sub-chunk k+1 (and k-1 for ks)
-    if (k >= 1) epilogue(k - 1, keep_du[ks], keep_g[ks]);
+    if (MODE == 0 && k >= 1) epilogue(k - 1, keep_du[ks], keep_g[ks]);
     prologue(k + 1, r_dl[rs], r_u[rs], r_z[rs], r_b[rs], r_c[rs], keep_du[ks], keep_g[ks]);
     // The refill must follow the slot's last use: hoisted above it, it would
     // need other registers and a copy at the loop edge that waits for it.
     // The zero below is produced only after every value of the slot and every
     // product of the prologue (so none of them is computed later from the
     // slot), and the refill's addresses depend on it.
-    const int zero = after_all(after_all(0, keep_du[ks], keep_g[ks]), r_dl[rs], r_u[rs], r_z[rs], r_b[rs],
-                               r_c[rs]);
+    int zero;
+    if constexpr (MODE == 0)
+      zero = after_all(after_all(0, keep_du[ks], keep_g[ks]), r_dl[rs], r_u[rs], r_z[rs], r_b[rs], r_c[rs]);
+    else
+      zero = after_all(0, r_dl[rs], r_u[rs], r_b[rs]);
     load_chunk(k + 1 + R + zero, r_dl[rs], r_u[rs], r_z[rs], r_b[rs], r_c[rs]);
     __syncthreads();
   };
@@ -616,6 +633,7 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < U - 1; ++i)
     if (k + i < nck) iteration(k + i, i);
+  if (MODE == 1) return;
   if ((nck - 1) & 1)
     epilogue(nck - 1, keep_du[1], keep_g[1]);
   else
@@ -714,22 +732,39 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   a.seg_hloc = ws;
   a.seg_state = ws + a.B * nseg * a.D * a.N;
   a.seg_dsum = ws + 2 * a.B * nseg * a.D * a.N;
-  hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 1, ZOH, FLAGS>), dim3(tiles, (unsigned)a.B, (unsigned)(nseg - 1)),
-                     dim3(64 * NW), 0, s, a);
+  // 16 states without the exact hold or the fused convolution: both passes
+  // run the wave-specialised kernel on 64-channel tiles
+  constexpr bool kWs = N == 16 && !ZOH;
+  const bool ws_ok = kWs && a.conv_k == 0;
+  const unsigned t64 = (unsigned)((a.D + 63) / 64);
+  if constexpr (kWs) {
+    if (ws_ok) {
+      const dim3 grid(t64, (unsigned)a.B, (unsigned)(nseg - 1));
+      if (a.flags)
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, 1>), grid,
+                           dim3(64 * (kWsRecWaves + 4)), 0, s, a);
+      else
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false, 1>), grid,
+                           dim3(64 * (kWsRecWaves + 4)), 0, s, a);
+    }
+  }
+  if (!ws_ok)
+    hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 1, ZOH, FLAGS>), dim3(tiles, (unsigned)a.B, (unsigned)(nseg - 1)),
+                       dim3(64 * NW), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nst = a.B * a.D * a.N;
   hipLaunchKernelGGL(fwd_seg_combine_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, a, nseg);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (N == 16 && !ZOH) {
-    if (a.conv_k == 0) {  // the segments' full scans: the wave-specialised kernel, 64-channel tiles
-      const dim3 grid((unsigned)((a.D + 63) / 64), (unsigned)a.B, (unsigned)nseg);
+  if constexpr (kWs) {
+    if (ws_ok) {  // the segments' full scans
+      const dim3 grid(t64, (unsigned)a.B, (unsigned)nseg);
       if (a.flags)
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true>), grid,
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, 0>), grid,
                            dim3(64 * (kWsRecWaves + 4)), 0, s, a);
       else
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false>), grid,
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false, 0>), grid,
                            dim3(64 * (kWsRecWaves + 4)), 0, s, a);
       return hipGetLastError();
     }
@@ -751,10 +786,10 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
     if (!(a.flags & kFlagZoh) && a.conv_k == 0 && pick_cpw<N>(a) == 64 && split_len(a.B, a.L, a.D) == 0) {
       const unsigned tiles = (unsigned)((a.D + 63) / 64);
       if (a.flags)
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true>), dim3(tiles, (unsigned)a.B, 1),
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, 0>), dim3(tiles, (unsigned)a.B, 1),
                            dim3(64 * (kWsRecWaves + 4)), 0, s, a);
       else
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false>), dim3(tiles, (unsigned)a.B, 1),
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false, 0>), dim3(tiles, (unsigned)a.B, 1),
                            dim3(64 * (kWsRecWaves + 4)), 0, s, a);
       return hipGetLastError();
     }

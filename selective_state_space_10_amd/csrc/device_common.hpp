@@ -123,4 +123,32 @@ __device__ __forceinline__ float step_size(float raw, float bias, bool softplus)
   return softplus ? softplus_f(s) : s;
 }
 
+// Returns z (always 0) through an opaque register move that reads every 32-bit
+// word of the given values: code whose operands depend on the result cannot be
+// scheduled before those values are computed and read.
+template <typename... Ts>
+__device__ __forceinline__ int after_all(int z, const Ts &...vals) {
+  constexpr int W = (0 + ... + (int)(sizeof(Ts) / 4));
+  uint32_t w[W];
+  int n = 0;
+  auto put = [&](const auto &v) {
+    static_assert(sizeof(v) % 4 == 0, "whole 32-bit words");
+    const auto *p = reinterpret_cast<const uint32_t *>(&v);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(v) / 4); ++i) w[n++] = p[i];
+  };
+  (put(vals), ...);
+#pragma unroll
+  for (int i = 0; i < W; i += 8) {  // eight words per move
+    auto at = [&](int k) { return w[i + k < W ? i + k : W - 1]; };
+    int out;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(out)
+                 : "v"(z), "v"(at(0)), "v"(at(1)), "v"(at(2)), "v"(at(3)), "v"(at(4)), "v"(at(5)),
+                   "v"(at(6)), "v"(at(7))
+                 : "memory");
+    z = out;
+  }
+  return z;
+}
+
 }  // namespace ssm

@@ -23,9 +23,10 @@ def ssm():
     return m
 
 
-@pytest.mark.parametrize("L", [1, 2, 31, 32, 33, 63, 64, 65])
+@pytest.mark.parametrize("L", [1, 2, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64, 65])
 def test_lengths_around_the_chunk(ssm, L):
-    """One chunk is 32 steps: lengths just below, at and above one and two chunks."""
+    """One chunk is 32 steps and the 16-state forward stages 16-step sub-chunks:
+    lengths just below, at and above one to four sub-chunks."""
     p = _problem(2, L, 72, 16, torch.float32, seed=L, h0=True)
     _check_fwd(ssm, p, 1e-4)
     _check_bwd(ssm, p, 1e-4, seed=L)

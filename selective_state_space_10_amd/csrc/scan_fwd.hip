@@ -342,7 +342,8 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
 
 // Forward with wave specialisation: 16 states, 64-channel tiles, no sequence
 // split; with FLAGS also the reverse direction, one step size per token and
-// accumulation into y (not the exact hold or the fused convolution).  MODE 1
+// accumulation into y, with ZOH the exact zero-order hold (not the fused
+// convolution).  MODE 1
 // is the first pass of a sequence split: each segment's end state from a zero
 // start and its sum of step sizes, no output.  NRW recurrence waves only run the recurrence, 16 / NRW
 // states per lane (lane = channel).  Four service waves do everything else
@@ -352,7 +353,7 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
 // T steps; LDS buffers alternate between sub-chunks, so one barrier per
 // sub-chunk orders everything.  On gfx950 plain arithmetic from one wave
 // fills issue slots that a recurrence wave on the same SIMD leaves free.
-template <typename IO, int NRW, int T, int R, bool FLAGS, int MODE>
+template <typename IO, int NRW, int T, int R, bool FLAGS, int MODE, bool ZOH>
 __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
   constexpr int N = 16, CPW = 64, SPL = N / NRW;
   constexpr int G = CPW / 4;        // 4-channel groups
@@ -387,7 +388,7 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
   const int64_t nck = (Ls + T - 1) / T;  // sub-chunks
   const int64_t K = (L + kChunkLen - 1) / kChunkLen;
 
-  __shared__ __attribute__((aligned(16))) float2 P[2][T][CPW];            // (dt, dt*u)
+  __shared__ __attribute__((aligned(16))) float2 P[2][T][CPW];            // (dt, dt*u), or (dt, u) with ZOH
   __shared__ __attribute__((aligned(16))) float BC[2][T][NRW][2 * SPL];  // B then C per recurrence wave
   __shared__ __attribute__((aligned(16))) float Y[2][T][NRW][64];        // per-lane partial sums
 
@@ -395,11 +396,13 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
     const int64_t d = d0 + lane;
     const bool dv = d < D;
     const int64_t dc = dv ? d : D - 1;
-    float Ap[SPL], h[SPL], dsum = 0.0f;
+    float Ap[SPL], An[SPL], Ainv[SPL], h[SPL], dsum = 0.0f;
 #pragma unroll
     for (int k = 0; k < SPL; ++k) {
       const int n = w * SPL + k;
-      Ap[k] = a.A[dc * N + n] * kLog2e;
+      An[k] = a.A[dc * N + n];
+      Ap[k] = An[k] * kLog2e;
+      Ainv[k] = ZOH ? 1.0f / An[k] : 0.0f;
       if (MODE == 1)
         h[k] = 0.0f;
       else if (a.seg_len)
@@ -428,7 +431,12 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
         for (int kk = 0; kk < SPL; ++kk) {
           const float da = fast_exp2(p.x * Ap[kk]);
-          h[kk] = fmaf(da, h[kk], p.y * bc[kk]);
+          if (ZOH) {  // p.y is u: the input coefficient expm1(dt A)/A depends on the state
+            const float cf = zoh_coef(p.x, p.x * An[kk], da, Ainv[kk]);
+            h[kk] = fmaf(da, h[kk], cf * p.y * bc[kk]);
+          } else {
+            h[kk] = fmaf(da, h[kk], p.y * bc[kk]);
+          }
           if (MODE == 0) ys = fmaf(bc[SPL + kk], h[kk], ys);
         }
         if (MODE == 0)
@@ -518,8 +526,13 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
         dt[q] = tv ? (sp ? sv : s) : 0.0f;
       }
       float4 *pp = (float4 *)&P[buf][tl][4 * g];
-      pp[0] = make_float4(dt[0], dt[0] * xv[0], dt[1], dt[1] * xv[1]);
-      pp[1] = make_float4(dt[2], dt[2] * xv[2], dt[3], dt[3] * xv[3]);
+      if (ZOH) {
+        pp[0] = make_float4(dt[0], xv[0], dt[1], xv[1]);
+        pp[1] = make_float4(dt[2], xv[2], dt[3], xv[3]);
+      } else {
+        pp[0] = make_float4(dt[0], dt[0] * xv[0], dt[1], dt[1] * xv[1]);
+        pp[1] = make_float4(dt[2], dt[2] * xv[2], dt[3], dt[3] * xv[3]);
+      }
       // D*u now rather than in the epilogue: a product, unlike u itself, is a
       // new value, so the raw slot can be refilled without a register copy
       // that would wait for the refill's loads.
@@ -704,19 +717,19 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   a.seg_hloc = ws;
   a.seg_state = ws + a.B * nseg * a.D * a.N;
   a.seg_dsum = ws + 2 * a.B * nseg * a.D * a.N;
-  // 16 states without the exact hold or the fused convolution: both passes
-  // run the wave-specialised kernel on 64-channel tiles
-  constexpr bool kWs = N == 16 && !ZOH;
+  // 16 states without the fused convolution: both passes run the
+  // wave-specialised kernel on 64-channel tiles
+  constexpr bool kWs = N == 16;
   const bool ws_ok = kWs && a.conv_k == 0;
   const unsigned t64 = (unsigned)((a.D + 63) / 64);
   if constexpr (kWs) {
     if (ws_ok) {
       const dim3 grid(t64, (unsigned)a.B, (unsigned)(nseg - 1));
       if (a.flags)
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, 1>), grid,
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, 1, ZOH>), grid,
                            dim3(64 * (kWsRecWaves + 4)), 0, s, a);
       else
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false, 1>), grid,
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false, 1, ZOH>), grid,
                            dim3(64 * (kWsRecWaves + 4)), 0, s, a);
     }
   }
@@ -733,10 +746,10 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
     if (ws_ok) {  // the segments' full scans
       const dim3 grid(t64, (unsigned)a.B, (unsigned)nseg);
       if (a.flags)
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, 0>), grid,
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, 0, ZOH>), grid,
                            dim3(64 * (kWsRecWaves + 4)), 0, s, a);
       else
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false, 0>), grid,
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false, 0, ZOH>), grid,
                            dim3(64 * (kWsRecWaves + 4)), 0, s, a);
       return hipGetLastError();
     }
@@ -755,14 +768,14 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
   if constexpr (N == 16) {
     // 64-channel tiles in one round over the CUs and no sequence split: the
     // wave-specialised kernel, also for the options it implements
-    if (!(a.flags & kFlagZoh) && a.conv_k == 0 && pick_cpw<N>(a) == 64 && split_len(a.B, a.L, a.D) == 0) {
-      const unsigned tiles = (unsigned)((a.D + 63) / 64);
-      if (a.flags)
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, 0>), dim3(tiles, (unsigned)a.B, 1),
-                           dim3(64 * (kWsRecWaves + 4)), 0, s, a);
+    if (a.conv_k == 0 && pick_cpw<N>(a) == 64 && split_len(a.B, a.L, a.D) == 0) {
+      const dim3 grid((unsigned)((a.D + 63) / 64), (unsigned)a.B, 1), block(64 * (kWsRecWaves + 4));
+      if (a.flags & kFlagZoh)
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, 0, true>), grid, block, 0, s, a);
+      else if (a.flags)
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, 0, false>), grid, block, 0, s, a);
       else
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false, 0>), dim3(tiles, (unsigned)a.B, 1),
-                           dim3(64 * (kWsRecWaves + 4)), 0, s, a);
+        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false, 0, false>), grid, block, 0, s, a);
       return hipGetLastError();
     }
   }

@@ -342,8 +342,8 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
 
 // Forward with wave specialisation: 16 states, 64-channel tiles, no sequence
 // split; with FLAGS also the reverse direction, one step size per token and
-// accumulation into y, with ZOH the exact zero-order hold (not the fused
-// convolution).  MODE 1
+// accumulation into y, with ZOH the exact zero-order hold, with CONV u built
+// by the fused causal convolution and SiLU from x (memory order).  MODE 1
 // is the first pass of a sequence split: each segment's end state from a zero
 // start and its sum of step sizes, no output.  NRW recurrence waves only run the recurrence, 16 / NRW
 // states per lane (lane = channel).  Four service waves do everything else
@@ -353,7 +353,7 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
 // T steps; LDS buffers alternate between sub-chunks, so one barrier per
 // sub-chunk orders everything.  On gfx950 plain arithmetic from one wave
 // fills issue slots that a recurrence wave on the same SIMD leaves free.
-template <typename IO, int NRW, int T, int R, bool FLAGS, int MODE, bool ZOH>
+template <typename IO, int NRW, int T, int R, bool FLAGS, int MODE, bool ZOH, bool CONV>
 __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
   constexpr int N = 16, CPW = 64, SPL = N / NRW;
   constexpr int G = CPW / 4;        // 4-channel groups
@@ -467,7 +467,10 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
   const bool gv = dg < D;  // D % 4 == 0: a group is all valid or all not
   const int64_t dgc = gv ? dg : D - 4;
   const bool has_z = a.z != nullptr;
-  const IO *__restrict__ zsrc = has_z ? zz : u;  // loaded either way, so no register slot is conditional
+  const IO *__restrict__ xin = (const IO *)a.x;
+  const IO *__restrict__ zsrc = has_z ? zz : CONV ? xin : u;  // loaded either way: no register slot is conditional
+  constexpr int XK = CONV ? kMaxConv : 1;
+  const int ck = CONV ? a.conv_k : 0;
   const bool sp = a.softplus != 0;
   const bool rev = FLAGS && (a.flags & kFlagReverse) != 0;
   const bool tok = FLAGS && (a.flags & kFlagDeltaPerToken) != 0;
@@ -476,6 +479,13 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
     return row0 + (rev ? L - 1 - (tb + t) : tb + t);
   };
   float bias4[4] = {0.f, 0.f, 0.f, 0.f}, Dsk4[4] = {0.f, 0.f, 0.f, 0.f};
+  float cw[4][XK], cb4[4] = {0.f, 0.f, 0.f, 0.f};  // convolution taps (zero past the width) and bias
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int kk = 0; kk < XK; ++kk) cw[q][kk] = CONV && kk < ck ? a.conv_w[(dgc + q) * ck + kk] : 0.0f;
+    if (CONV && a.conv_b) cb4[q] = a.conv_b[dgc + q];
+  }
   if (a.bias) {
     const float4 v = *(const float4 *)(a.bias + dgc);
     bias4[0] = v.x, bias4[1] = v.y, bias4[2] = v.z, bias4[3] = v.w;
@@ -486,18 +496,28 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
   }
 
   raw_t r_dl[R][IPT], r_u[R][IPT], r_z[R][IPT];  // loads in flight: sub-chunk j in slot j % R
+  raw_t r_x[R][IPT][XK];                          // with CONV: the rows of x the convolution reads
   float r_b[R][BPT], r_c[R][BPT];
   float4 keep_du[2][IPT], keep_g[2][IPT];         // D*u and silu(z), by sub-chunk parity
 
   auto load_chunk = [&](int64_t k, raw_t(&ra)[IPT], raw_t(&ru)[IPT], raw_t(&rz)[IPT], float(&rb)[BPT],
-                        float(&rc)[BPT]) {
+                        float(&rc)[BPT], raw_t(&rx)[IPT][XK]) {
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int64_t t = k * T + tl0 + j * (NV / G);
       const int64_t r = mrow(t < Ls ? t : Ls - 1);
       const int64_t idx = r * D + dgc;
       ra[j] = tok ? V::splat(dl, r) : V::load(dl, idx);
-      ru[j] = V::load(u, idx);
+      if (CONV) {  // rows r-(K-1) .. r, clamped into the sequence (rows before 0 are zeroed later)
+#pragma unroll
+        for (int kk = 0; kk < XK; ++kk) {
+          int64_t ts = r - row0 - (ck - 1) + kk;
+          ts = ts < 0 ? 0 : ts < L ? ts : L - 1;
+          rx[j][kk] = V::load(xin, (row0 + ts) * D + dgc);
+        }
+      } else {
+        ru[j] = V::load(u, idx);
+      }
       if (MODE == 0) rz[j] = V::load(zsrc, idx);
     }
 #pragma unroll
@@ -510,13 +530,31 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
     }
   };
   auto prologue = [&](int64_t k, raw_t(&ra)[IPT], raw_t(&ru)[IPT], raw_t(&rz)[IPT], float(&rb)[BPT],
-                      float(&rc)[BPT], float4(&kdu)[IPT], float4(&kg)[IPT]) {
+                      float(&rc)[BPT], raw_t(&rx)[IPT][XK], float4(&kdu)[IPT], float4(&kg)[IPT]) {
     const int buf = (int)(k & 1);
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int tl = tl0 + j * (NV / G);
       const bool tv = k * T + tl < Ls;  // steps past the end get dt = 0: no state change
-      const float4 r = V::cvt(ra[j]), x = V::cvt(ru[j]);
+      const float4 r = V::cvt(ra[j]);
+      float4 x;
+      if (CONV) {  // u = silu(bias + sum_k w_k x[t - (K-1) + k]), x = 0 before the first row
+        const int64_t tm = tb + (k * T + tl < Ls ? k * T + tl : Ls - 1);
+        float pre[4] = {cb4[0], cb4[1], cb4[2], cb4[3]};
+#pragma unroll
+        for (int kk = 0; kk < XK; ++kk) {
+          const bool inb = tm - (ck - 1) + kk >= 0;
+          const float4 xr = V::cvt(rx[j][kk]);
+          const float4 xv = inb ? xr : make_float4(0.f, 0.f, 0.f, 0.f);
+          pre[0] = fmaf(cw[0][kk], xv.x, pre[0]);
+          pre[1] = fmaf(cw[1][kk], xv.y, pre[1]);
+          pre[2] = fmaf(cw[2][kk], xv.z, pre[2]);
+          pre[3] = fmaf(cw[3][kk], xv.w, pre[3]);
+        }
+        x = make_float4(silu_f(pre[0]), silu_f(pre[1]), silu_f(pre[2]), silu_f(pre[3]));
+      } else {
+        x = V::cvt(ru[j]);
+      }
       const float rv[4] = {r.x, r.y, r.z, r.w}, xv[4] = {x.x, x.y, x.z, x.w};
       float dt[4];
 #pragma unroll
@@ -585,9 +623,9 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
   // unconditionally: a register slot that is only sometimes refilled would
   // make the compiler copy it and wait for loads still in flight.
 #pragma unroll
-  for (int j = 0; j < R; ++j) load_chunk(j, r_dl[j], r_u[j], r_z[j], r_b[j], r_c[j]);
-  prologue(0, r_dl[0], r_u[0], r_z[0], r_b[0], r_c[0], keep_du[0], keep_g[0]);
-  load_chunk(R, r_dl[0], r_u[0], r_z[0], r_b[0], r_c[0]);
+  for (int j = 0; j < R; ++j) load_chunk(j, r_dl[j], r_u[j], r_z[j], r_b[j], r_c[j], r_x[j]);
+  prologue(0, r_dl[0], r_u[0], r_z[0], r_b[0], r_c[0], r_x[0], keep_du[0], keep_g[0]);
+  load_chunk(R, r_dl[0], r_u[0], r_z[0], r_b[0], r_c[0], r_x[0]);
   __syncthreads();  // sub-chunk 0 staged
   // Iteration k (the recurrence waves scan sub-chunk k): epilogue of k-1,
   // then prologue of k+1 and the loads of k+1+R into the slot it frees.
@@ -596,18 +634,18 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
   auto iteration = [&](int64_t k, const int i) {  // i = k % U
     const int rs = (i + 1) % R, ks = (i + 1) % 2;  // slots of sub-chunk k+1 (and k-1 for ks)
     if (MODE == 0 && k >= 1) epilogue(k - 1, keep_du[ks], keep_g[ks]);
-    prologue(k + 1, r_dl[rs], r_u[rs], r_z[rs], r_b[rs], r_c[rs], keep_du[ks], keep_g[ks]);
+    prologue(k + 1, r_dl[rs], r_u[rs], r_z[rs], r_b[rs], r_c[rs], r_x[rs], keep_du[ks], keep_g[ks]);
     // The refill must follow the slot's last use: hoisted above it, it would
     // need other registers and a copy at the loop edge that waits for it.
     // The zero below is produced only after every value of the slot and every
     // product of the prologue (so none of them is computed later from the
     // slot), and the refill's addresses depend on it.
-    int zero;
-    if constexpr (MODE == 0)
-      zero = after_all(after_all(0, keep_du[ks], keep_g[ks]), r_dl[rs], r_u[rs], r_z[rs], r_b[rs], r_c[rs]);
+    int zero = MODE == 0 ? after_all(0, keep_du[ks], keep_g[ks], r_z[rs], r_c[rs]) : 0;
+    if constexpr (CONV)
+      zero = after_all(zero, r_dl[rs], r_x[rs], r_b[rs]);
     else
-      zero = after_all(0, r_dl[rs], r_u[rs], r_b[rs]);
-    load_chunk(k + 1 + R + zero, r_dl[rs], r_u[rs], r_z[rs], r_b[rs], r_c[rs]);
+      zero = after_all(zero, r_dl[rs], r_u[rs], r_b[rs]);
+    load_chunk(k + 1 + R + zero, r_dl[rs], r_u[rs], r_z[rs], r_b[rs], r_c[rs], r_x[rs]);
     __syncthreads();
   };
   int64_t k = 0;
@@ -630,6 +668,18 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
 // with 16-step sub-chunks beat four (one per SIMD) with 32-step ones, and a
 // ring of two register slots beats four (which spills).
 constexpr int kWsRecWaves = 8, kWsSteps = 16, kWsRing = 2;
+
+// Launches the wave-specialised forward variant for the arguments' options.
+template <typename IO, int MODE, bool ZOH>
+static void launch_ws(const FwdArgs &a, dim3 grid, hipStream_t s) {
+  const dim3 block(64 * (kWsRecWaves + 4));
+  if (a.conv_k)
+    hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, MODE, ZOH, true>), grid, block, 0, s, a);
+  else if (a.flags)
+    hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, MODE, ZOH, false>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false, MODE, ZOH, false>), grid, block, 0, s, a);
+}
 
 // Second phase of a sequence split: the state entering every segment,
 // h_in[0] = h0, h_in[s+1] = exp(A * sum of dt over s) * h_in[s] + h_loc[s]
@@ -717,23 +767,12 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   a.seg_hloc = ws;
   a.seg_state = ws + a.B * nseg * a.D * a.N;
   a.seg_dsum = ws + 2 * a.B * nseg * a.D * a.N;
-  // 16 states without the fused convolution: both passes run the
-  // wave-specialised kernel on 64-channel tiles
+  // 16 states: both passes run the wave-specialised kernel on 64-channel tiles
   constexpr bool kWs = N == 16;
-  const bool ws_ok = kWs && a.conv_k == 0;
   const unsigned t64 = (unsigned)((a.D + 63) / 64);
-  if constexpr (kWs) {
-    if (ws_ok) {
-      const dim3 grid(t64, (unsigned)a.B, (unsigned)(nseg - 1));
-      if (a.flags)
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, 1, ZOH>), grid,
-                           dim3(64 * (kWsRecWaves + 4)), 0, s, a);
-      else
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false, 1, ZOH>), grid,
-                           dim3(64 * (kWsRecWaves + 4)), 0, s, a);
-    }
-  }
-  if (!ws_ok)
+  if constexpr (kWs)
+    launch_ws<IO, 1, ZOH>(a, dim3(t64, (unsigned)a.B, (unsigned)(nseg - 1)), s);
+  else
     hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 1, ZOH, FLAGS>), dim3(tiles, (unsigned)a.B, (unsigned)(nseg - 1)),
                        dim3(64 * NW), 0, s, a);
   hipError_t e = hipGetLastError();
@@ -742,17 +781,9 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   hipLaunchKernelGGL(fwd_seg_combine_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, a, nseg);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (kWs) {
-    if (ws_ok) {  // the segments' full scans
-      const dim3 grid(t64, (unsigned)a.B, (unsigned)nseg);
-      if (a.flags)
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, 0, ZOH>), grid,
-                           dim3(64 * (kWsRecWaves + 4)), 0, s, a);
-      else
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false, 0, ZOH>), grid,
-                           dim3(64 * (kWsRecWaves + 4)), 0, s, a);
-      return hipGetLastError();
-    }
+  if constexpr (kWs) {  // the segments' full scans
+    launch_ws<IO, 0, ZOH>(a, dim3(t64, (unsigned)a.B, (unsigned)nseg), s);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0, ZOH, FLAGS>), dim3(tiles, (unsigned)a.B, (unsigned)nseg),
                      dim3(64 * NW), 0, s, a);
@@ -768,14 +799,12 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
   if constexpr (N == 16) {
     // 64-channel tiles in one round over the CUs and no sequence split: the
     // wave-specialised kernel, also for the options it implements
-    if (a.conv_k == 0 && pick_cpw<N>(a) == 64 && split_len(a.B, a.L, a.D) == 0) {
-      const dim3 grid((unsigned)((a.D + 63) / 64), (unsigned)a.B, 1), block(64 * (kWsRecWaves + 4));
+    if (pick_cpw<N>(a) == 64 && split_len(a.B, a.L, a.D) == 0) {
+      const dim3 grid((unsigned)((a.D + 63) / 64), (unsigned)a.B, 1);
       if (a.flags & kFlagZoh)
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, 0, true>), grid, block, 0, s, a);
-      else if (a.flags)
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, 0, false>), grid, block, 0, s, a);
+        launch_ws<IO, 0, true>(a, grid, s);
       else
-        hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false, 0, false>), grid, block, 0, s, a);
+        launch_ws<IO, 0, false>(a, grid, s);
       return hipGetLastError();
     }
   }

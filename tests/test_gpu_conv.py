@@ -49,7 +49,8 @@ def _gpu_fwd(ssm, p, zoh=False, **kw):
 @pytest.mark.parametrize("B,L,D,N,dtype,K", [
     (2, 300, 72, 16, torch.float32, 4), (2, 300, 72, 16, torch.bfloat16, 4),
     (3, 97, 136, 8, torch.float32, 3), (2, 45, 64, 1, torch.float32, 2),
-    (1, 70, 16, 2, torch.bfloat16, 1), (1, 3, 8, 4, torch.float32, 4)])
+    (1, 70, 16, 2, torch.bfloat16, 1), (1, 3, 8, 4, torch.float32, 4),
+    (2, 100, 64, 16, torch.float32, 2), (1, 50, 72, 16, torch.bfloat16, 1), (1, 2, 64, 16, torch.float32, 3)])
 @pytest.mark.parametrize("opts", [dict(), dict(zoh=True, tok=True, bias=False)], ids=["plain", "zoh-tok"])
 def test_fwd_conv_small(ssm, B, L, D, N, dtype, K, opts):
     opts = dict(opts)  # the parametrised dict is shared between cases

@@ -8,7 +8,18 @@
 // "Donanım Duyarlı Durum Genişletme" section: the expanded state is never
 // materialised in device memory).
 //
-// One workgroup owns 64 consecutive channels of one batch row and walks the
+// Two kernels share this file.
+//
+// fwd_ws_kernel (16 states, 64-channel tiles; every option and both passes of
+// a sequence split) specialises waves: eight recurrence waves, two per SIMD,
+// only run the recurrence (lane = channel, two states per lane); four service
+// waves load the inputs a few 16-step sub-chunks ahead, stage (dt, dt*u) and
+// B/C in LDS, and sum, gate and store the outputs.  A SIMD issues a service
+// wave's plain arithmetic in the slots its recurrence waves leave free.
+//
+// fwd_kernel (other state sizes, and 32-channel tiles when 64-channel tiles
+// would need a second round over the CUs) runs every phase on every wave.
+// One workgroup owns CPW consecutive channels of one batch row and walks the
 // sequence in chunks of T steps:
 //   - Cooperative phases (all threads): every thread owns fixed (step, group of
 //     4 channels) items of a chunk and moves them with 16-byte (fp32) or
@@ -16,10 +27,9 @@
 //     and stores them in LDS once per (t, d); it also stages the chunk's B and
 //     C rows in LDS.  The epilogue adds the per-wave partial sums, applies
 //     D*u and the SiLU gate, and stores y.
-//   - Recurrence (one wave per NPL states): lanes are channels, so the 2-state
-//     slices of the 16-state problem put 8 waves (2 per SIMD) on the 64
-//     channels.  Each step reads (dt, dt*u) for its lane and the wave's
-//     B/C values from LDS, updates the states, and leaves sum_n C h in LDS.
+//   - Recurrence (one wave per NPL states): lanes are channels, and each step
+//     reads (dt, dt*u) for its lane and the wave's B/C values from LDS,
+//     updates the states, and leaves sum_n C h in LDS.
 //   - Loads run PD chunks ahead in registers, so that several chunks of
 //     input are in flight while the recurrence of the current one executes.
 #include <stdlib.h>

@@ -350,27 +350,36 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
   }
 }
 
-// Forward with wave specialisation: 16 states, 64-channel tiles, no sequence
-// split; with FLAGS also the reverse direction, one step size per token and
-// accumulation into y, with ZOH the exact zero-order hold, with CONV u built
-// by the fused causal convolution and SiLU from x (memory order).  MODE 1
-// is the first pass of a sequence split: each segment's end state from a zero
-// start and its sum of step sizes, no output.  NRW recurrence waves only run the recurrence, 16 / NRW
-// states per lane (lane = channel).  Four service waves do everything else
-// for the same tile: global loads a few sub-chunks ahead, the step-size
-// prologue and B/C staging of the next sub-chunk, and the epilogue (sum of
-// the NRW partials, D*u, gate, store) of the previous one.  A sub-chunk is
-// T steps; LDS buffers alternate between sub-chunks, so one barrier per
-// sub-chunk orders everything.  On gfx950 plain arithmetic from one wave
-// fills issue slots that a recurrence wave on the same SIMD leaves free.
-template <typename IO, int NRW, int T, int R, bool FLAGS, int MODE, bool ZOH, bool CONV>
-__global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
-  constexpr int N = 16, CPW = 64, SPL = N / NRW;
+// Forward with wave specialisation: 16 states, tiles of CPW = 64 or 32
+// channels of one batch row, optionally one segment of a split sequence.  With
+// FLAGS also the reverse direction, one step size per token and accumulation
+// into y, with ZOH the exact zero-order hold, with CONV u built by the fused
+// causal convolution and SiLU from x (memory order).  MODE 1 is the first pass
+// of a sequence split: each segment's end state from a zero start and its sum
+// of step sizes, no output.
+// The recurrence waves only run the recurrence, two states per lane.  The
+// service waves (one per 16 channels) do everything else for the same tile:
+// global loads a few sub-chunks ahead, the step-size prologue and B/C staging
+// of the next sub-chunk, and the epilogue (sum of the eight partials, D*u,
+// gate, store) of the previous one.  A sub-chunk is T steps; LDS buffers
+// alternate between sub-chunks, so one barrier per sub-chunk orders
+// everything.  On gfx950 plain arithmetic from one wave fills issue slots
+// that a recurrence wave on the same SIMD leaves free.
+template <typename IO, int CPW, int T, int R, bool FLAGS, int MODE, bool ZOH, bool CONV>
+__global__ void __launch_bounds__(64 * (CPW / 8 + CPW / 16)) __attribute__((amdgpu_waves_per_eu(CPW == 32 ? 4 : 1)))
+fwd_ws_kernel(FwdArgs a) {
+  // CPW = 64: lane = channel, 8 recurrence waves, 4 service waves, one
+  // workgroup per CU.  CPW = 32: lane = channel + 32 * (state half), 4
+  // recurrence waves, 2 service waves, two workgroups per CU (at most four
+  // waves per SIMD: with five, the register bound makes the service waves
+  // spill and the 2.8b shape runs 17% slower).  Either way eight state slices
+  // of 2 states.
+  constexpr int N = 16, NRW = CPW / 8, NSV = CPW / 16, NVW = 8, SPL = N / NVW;
   constexpr int G = CPW / 4;        // 4-channel groups
-  constexpr int NV = 256;           // service threads
+  constexpr int NV = 64 * NSV;      // service threads
   constexpr int IPT = T * G / NV;   // (step, channel group) items per service thread
   constexpr int BPT = T * N / NV;   // B and C values per service thread
-  static_assert(SPL * NRW == N && SPL % 2 == 0, "states split evenly, B/C in float4 pieces");
+  static_assert((CPW == 64 || CPW == 32) && SPL % 2 == 0, "B/C in float4 pieces");
   static_assert(IPT >= 1 && BPT >= 1 && kChunkLen % T == 0, "sub-chunks tile the chunk");
   using V = Vec4<IO>;
   typedef typename V::raw raw_t;
@@ -399,17 +408,19 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
   const int64_t K = (L + kChunkLen - 1) / kChunkLen;
 
   __shared__ __attribute__((aligned(16))) float2 P[2][T][CPW];            // (dt, dt*u), or (dt, u) with ZOH
-  __shared__ __attribute__((aligned(16))) float BC[2][T][NRW][2 * SPL];  // B then C per recurrence wave
-  __shared__ __attribute__((aligned(16))) float Y[2][T][NRW][64];        // per-lane partial sums
+  __shared__ __attribute__((aligned(16))) float BC[2][T][NVW][2 * SPL];  // B then C per state slice
+  __shared__ __attribute__((aligned(16))) float Y[2][T][NVW][CPW];       // per-lane partial sums
 
   if (w < NRW) {  // ------------------------------------------- recurrence waves
-    const int64_t d = d0 + lane;
+    const int cl = lane % CPW;                   // channel in the tile
+    const int vw = w * (64 / CPW) + lane / CPW;  // state slice: states vw*SPL ..
+    const int64_t d = d0 + cl;
     const bool dv = d < D;
     const int64_t dc = dv ? d : D - 1;
     float Ap[SPL], An[SPL], Ainv[SPL], h[SPL], dsum = 0.0f;
 #pragma unroll
     for (int k = 0; k < SPL; ++k) {
-      const int n = w * SPL + k;
+      const int n = vw * SPL + k;
       An[k] = a.A[dc * N + n];
       Ap[k] = An[k] * kLog2e;
       Ainv[k] = ZOH ? 1.0f / An[k] : 0.0f;
@@ -424,17 +435,17 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
     for (int64_t k = 0; k < nck; ++k) {
       const int buf = (int)(k & 1);
       if (MODE == 0 && a.chunk_states && dv && (k * T) % kChunkLen == 0) {  // tb is a multiple of kChunkLen
-        float *cs = a.chunk_states + ((b * K + (tb + k * T) / kChunkLen) * N + w * SPL) * D + d;
+        float *cs = a.chunk_states + ((b * K + (tb + k * T) / kChunkLen) * N + vw * SPL) * D + d;
 #pragma unroll
         for (int kk = 0; kk < SPL; ++kk) cs[kk * D] = h[kk];
       }
 #pragma unroll
       for (int tl = 0; tl < T; ++tl) {
-        const float2 p = P[buf][tl][lane];
+        const float2 p = P[buf][tl][cl];
         float bc[2 * SPL];
 #pragma unroll
         for (int i = 0; i < SPL / 2; ++i) {
-          const float4 q = *(const float4 *)&BC[buf][tl][w][4 * i];
+          const float4 q = *(const float4 *)&BC[buf][tl][vw][4 * i];
           bc[4 * i] = q.x, bc[4 * i + 1] = q.y, bc[4 * i + 2] = q.z, bc[4 * i + 3] = q.w;
         }
         float ys = 0.0f;
@@ -450,7 +461,7 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
           if (MODE == 0) ys = fmaf(bc[SPL + kk], h[kk], ys);
         }
         if (MODE == 0)
-          Y[buf][tl][w][lane] = ys;
+          Y[buf][tl][vw][cl] = ys;
         else
           dsum += p.x;
       }
@@ -459,12 +470,12 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
     if (MODE == 1) {
       if (dv) {
 #pragma unroll
-        for (int kk = 0; kk < SPL; ++kk) a.seg_hloc[((b * nseg + seg) * D + d) * N + w * SPL + kk] = h[kk];
-        if (w == 0) a.seg_dsum[(b * nseg + seg) * D + d] = dsum;
+        for (int kk = 0; kk < SPL; ++kk) a.seg_hloc[((b * nseg + seg) * D + d) * N + vw * SPL + kk] = h[kk];
+        if (vw == 0) a.seg_dsum[(b * nseg + seg) * D + d] = dsum;
       }
     } else if (a.h_final && dv && tb + Ls == L) {
 #pragma unroll
-      for (int kk = 0; kk < SPL; ++kk) a.h_final[(b * D + d) * N + w * SPL + kk] = h[kk];
+      for (int kk = 0; kk < SPL; ++kk) a.h_final[(b * D + d) * N + vw * SPL + kk] = h[kk];
     }
     return;  // the service waves' last epilogue needs no further barrier
   }
@@ -610,7 +621,7 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
       if (t < Ls && gv) {
         float4 s = *(const float4 *)&Y[buf][tl][0][4 * g];
 #pragma unroll
-        for (int ww = 1; ww < NRW; ++ww) {
+        for (int ww = 1; ww < NVW; ++ww) {
           const float4 v = *(const float4 *)&Y[buf][tl][ww][4 * g];
           s.x += v.x, s.y += v.y, s.z += v.z, s.w += v.w;
         }
@@ -677,18 +688,18 @@ __global__ void __launch_bounds__(64 * (NRW + 4)) fwd_ws_kernel(FwdArgs a) {
 // 2048 x 16 (fp32): eight recurrence waves (two per SIMD, 2 states per lane)
 // with 16-step sub-chunks beat four (one per SIMD) with 32-step ones, and a
 // ring of two register slots beats four (which spills).
-constexpr int kWsRecWaves = 8, kWsSteps = 16, kWsRing = 2;
+constexpr int kWsSteps = 16, kWsRing = 2;
 
 // Launches the wave-specialised forward variant for the arguments' options.
-template <typename IO, int MODE, bool ZOH>
+template <typename IO, int CPW, int MODE, bool ZOH>
 static void launch_ws(const FwdArgs &a, dim3 grid, hipStream_t s) {
-  const dim3 block(64 * (kWsRecWaves + 4));
+  const dim3 block(64 * (CPW / 8 + CPW / 16));
   if (a.conv_k)
-    hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, MODE, ZOH, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((fwd_ws_kernel<IO, CPW, kWsSteps, kWsRing, true, MODE, ZOH, true>), grid, block, 0, s, a);
   else if (a.flags)
-    hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, true, MODE, ZOH, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((fwd_ws_kernel<IO, CPW, kWsSteps, kWsRing, true, MODE, ZOH, false>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_ws_kernel<IO, kWsRecWaves, kWsSteps, kWsRing, false, MODE, ZOH, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((fwd_ws_kernel<IO, CPW, kWsSteps, kWsRing, false, MODE, ZOH, false>), grid, block, 0, s, a);
 }
 
 // Second phase of a sequence split: the state entering every segment,
@@ -781,7 +792,7 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   constexpr bool kWs = N == 16;
   const unsigned t64 = (unsigned)((a.D + 63) / 64);
   if constexpr (kWs)
-    launch_ws<IO, 1, ZOH>(a, dim3(t64, (unsigned)a.B, (unsigned)(nseg - 1)), s);
+    launch_ws<IO, 64, 1, ZOH>(a, dim3(t64, (unsigned)a.B, (unsigned)(nseg - 1)), s);
   else
     hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 1, ZOH, FLAGS>), dim3(tiles, (unsigned)a.B, (unsigned)(nseg - 1)),
                        dim3(64 * NW), 0, s, a);
@@ -792,7 +803,7 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (kWs) {  // the segments' full scans
-    launch_ws<IO, 0, ZOH>(a, dim3(t64, (unsigned)a.B, (unsigned)nseg), s);
+    launch_ws<IO, 64, 0, ZOH>(a, dim3(t64, (unsigned)a.B, (unsigned)nseg), s);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0, ZOH, FLAGS>), dim3(tiles, (unsigned)a.B, (unsigned)nseg),
@@ -809,12 +820,15 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
   if constexpr (N == 16) {
     // 64-channel tiles in one round over the CUs and no sequence split: the
     // wave-specialised kernel, also for the options it implements
-    if (pick_cpw<N>(a) == 64 && split_len(a.B, a.L, a.D) == 0) {
-      const dim3 grid((unsigned)((a.D + 63) / 64), (unsigned)a.B, 1);
-      if (a.flags & kFlagZoh)
-        launch_ws<IO, 0, true>(a, grid, s);
-      else
-        launch_ws<IO, 0, false>(a, grid, s);
+    if (split_len(a.B, a.L, a.D) == 0) {
+      const bool zoh = (a.flags & kFlagZoh) != 0;
+      if (pick_cpw<N>(a) == 64) {
+        const dim3 grid((unsigned)((a.D + 63) / 64), (unsigned)a.B, 1);
+        zoh ? launch_ws<IO, 64, 0, true>(a, grid, s) : launch_ws<IO, 64, 0, false>(a, grid, s);
+      } else {  // 32-channel tiles: several workgroups per CU
+        const dim3 grid((unsigned)((a.D + 31) / 32), (unsigned)a.B, 1);
+        zoh ? launch_ws<IO, 32, 0, true>(a, grid, s) : launch_ws<IO, 32, 0, false>(a, grid, s);
+      }
       return hipGetLastError();
     }
   }

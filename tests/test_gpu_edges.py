@@ -44,6 +44,18 @@ def test_small_channel_counts_and_short_rows(ssm, B, L, D, N, dtype):
     _check_bwd(ssm, p, TOL[dtype], seed=B)
 
 
+@pytest.mark.parametrize("opts", [dict(), dict(zoh=True), dict(reverse=True, tok=True)],
+                         ids=["plain", "zoh", "reverse-per-token"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_many_channel_tiles(ssm, dtype, opts):
+    """More 64-channel tiles than compute units (5 rows x 53 tiles): the
+    16-state forward switches to 32-channel tiles, the last one ragged (8 of
+    32 channels)."""
+    from tests.test_gpu_options import _check_fwd as _check_fwd_opts, _with_opts
+    p = _with_opts(_problem(5, 40, 3336, 16, dtype, seed=41, h0=True), opts.get("tok", False))
+    _check_fwd_opts(ssm, p, TOL[dtype], opts.get("zoh", False), opts.get("reverse", False))
+
+
 def test_nan_propagates_in_its_channel_only(ssm):
     """A NaN input poisons its own channel from that step on (through the
     state) and nothing else: channels are independent recurrences."""

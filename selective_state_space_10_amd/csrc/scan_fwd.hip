@@ -10,15 +10,14 @@
 //
 // Two kernels share this file.
 //
-// fwd_ws_kernel (16 states, 64-channel tiles; every option and both passes of
-// a sequence split) specialises waves: eight recurrence waves, two per SIMD,
-// only run the recurrence (lane = channel, two states per lane); four service
-// waves load the inputs a few 16-step sub-chunks ahead, stage (dt, dt*u) and
-// B/C in LDS, and sum, gate and store the outputs.  A SIMD issues a service
-// wave's plain arithmetic in the slots its recurrence waves leave free.
+// fwd_ws_kernel (16 states, 64- or 32-channel tiles; every option and both
+// passes of a sequence split) specialises waves: recurrence waves only run the
+// recurrence (two states per lane); service waves load the inputs a few
+// 16-step sub-chunks ahead, stage (dt, dt*u) and B/C in LDS, and sum, gate and
+// store the outputs.  A SIMD issues a service wave's plain arithmetic in the
+// slots its recurrence waves leave free.
 //
-// fwd_kernel (other state sizes, and 32-channel tiles when 64-channel tiles
-// would need a second round over the CUs) runs every phase on every wave.
+// fwd_kernel (1, 2, 4 or 8 states) runs every phase on every wave.
 // One workgroup owns CPW consecutive channels of one batch row and walks the
 // sequence in chunks of T steps:
 //   - Cooperative phases (all threads): every thread owns fixed (step, group of

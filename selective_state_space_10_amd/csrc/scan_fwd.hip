@@ -736,11 +736,11 @@ static int64_t split_len(int64_t B, int64_t L, int64_t D) {
   return len;
 }
 
-// Channels per workgroup (CPW) for dstate N.  A 64-channel tile needs 84 KB
-// of LDS (one workgroup per CU); 32- and 16-channel tiles fit 3 and 6 per CU.
-// Measured on MI355X: 64-channel tiles are fastest while the grid fits in one
-// round over the CUs; beyond that, 32-channel tiles avoid a mostly idle
-// second round.  SSM_FWD_CPW overrides the choice (tuning only).
+// Channels per workgroup (CPW) for dstate N.  A 64-channel tile takes a CU
+// (84 KB of LDS); 32-channel tiles fit two (16 states) or three (fwd_kernel)
+// per CU.  Measured on MI355X: 64-channel tiles are fastest while the grid
+// fits in one round over the CUs; beyond that, 32-channel tiles avoid a
+// mostly idle second round.  SSM_FWD_CPW overrides the choice (tuning only).
 static int device_cus() {
   static int cus = [] {
     int dev = 0, n = 0;

@@ -66,11 +66,14 @@ def test_fwd_conv_small(ssm, B, L, D, N, dtype, K, opts):
     assert nmax_err(cs.permute(0, 1, 3, 2), cso) <= tol
 
 
-def test_fwd_conv_sequence_split(ssm):
+@pytest.mark.parametrize("zoh", [False, True])
+def test_fwd_conv_sequence_split(ssm, zoh):
+    """A split sequence: segments read the convolution rows of the segment
+    before them."""
     p = _conv_problem(1, 10000, 16, 16, torch.float32, 4, seed=3)
-    y, hf, _ = _gpu_fwd(ssm, _to(p, "cuda"), return_final_state=True)
+    y, hf, _ = _gpu_fwd(ssm, _to(p, "cuda"), zoh, return_final_state=True)
     torch.cuda.synchronize()
-    yo, hfo, _ = oracle_c.scan_fwd_conv(**_okw(p))
+    yo, hfo, _ = oracle_c.scan_fwd_conv(**_okw(p), zoh=zoh)
     assert nmax_err(y, yo) <= 1e-4 and nmax_err(hf, hfo) <= 1e-4
 
 

@@ -92,6 +92,20 @@ def test_fwd_accumulate_and_bidirectional(ssm, dtype):
     assert nmax_err(yb, yf + yr) <= TOL[dtype] * (1 if dtype == torch.float32 else 1.5)
 
 
+def test_bidirectional_sequence_split(ssm):
+    """Both directions over a split sequence (the reverse launch accumulates
+    into y)."""
+    p = _problem(1, 10000, 16, 16, torch.float32, seed=13)
+    pg = _to(p, "cuda")
+    yb = ssm.bidirectional_scan(pg["u"], pg["delta"], pg["A"], pg["B"], pg["C"], pg["D"], pg["z"],
+                                pg["delta_bias"], True)
+    torch.cuda.synchronize()
+    ok = _oracle_kwargs(p)
+    yf, _, _ = oracle_c.scan_fwd(**ok)
+    yr, _, _ = oracle_c.scan_fwd(**dict(ok, D=None), reverse=True)
+    assert nmax_err(yb, yf + yr) <= TOL[torch.float32]
+
+
 def test_fwd_zoh_workload1_full_size(ssm):
     """The Mamba-370m shape with the exact hold, on sampled channels."""
     w = WORKLOADS[1]

@@ -10,7 +10,7 @@
 //
 // Two kernels share this file.
 //
-// fwd_ws_kernel (16 states, 64- or 32-channel tiles; every option and both
+// fwd_ws_kernel (16 states, 64-, 80- or 32-channel tiles; every option and both
 // passes of a sequence split) specialises waves: recurrence waves only run the
 // recurrence (two states per lane); service waves load the inputs a few
 // 16-step sub-chunks ahead, stage (dt, dt*u) and B/C in LDS, and sum, gate and
@@ -349,7 +349,7 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
   }
 }
 
-// Forward with wave specialisation: 16 states, tiles of CPW = 64 or 32
+// Forward with wave specialisation: 16 states, tiles of CPW = 64, 80 or 32
 // channels of one batch row, optionally one segment of a split sequence.  With
 // FLAGS also the reverse direction, one step size per token and accumulation
 // into y, with ZOH the exact zero-order hold, with CONV u built by the fused
@@ -367,19 +367,21 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
 template <typename IO, int CPW, int T, int R, bool FLAGS, int MODE, bool ZOH, bool CONV>
 __global__ void __launch_bounds__(64 * (CPW / 8 + CPW / 16)) __attribute__((amdgpu_waves_per_eu(CPW == 32 ? 4 : 1)))
 fwd_ws_kernel(FwdArgs a) {
-  // CPW = 64: lane = channel, 8 recurrence waves, 4 service waves, one
-  // workgroup per CU.  CPW = 32: lane = channel + 32 * (state half), 4
-  // recurrence waves, 2 service waves, two workgroups per CU (at most four
-  // waves per SIMD: with five, the register bound makes the service waves
-  // spill and the 2.8b shape runs 17% slower).  Either way eight state slices
-  // of 2 states.
+  // Recurrence thread r (of 8 * CPW) holds channel r % CPW of state slice
+  // r / CPW; eight slices of 2 states.  CPW = 64: 8 recurrence waves, 4
+  // service waves, one workgroup per CU.  CPW = 80: 10 and 5 waves, one
+  // workgroup per CU (at most four waves per SIMD, so 128 registers); for
+  // channel counts like 5120 whose 64-channel tiles would leave a second,
+  // mostly idle round over the CUs.  CPW = 32: 4 and 2 waves, two workgroups
+  // per CU (at most four waves per SIMD: with five, the register bound makes
+  // the service waves spill and the 2.8b shape runs 17% slower).
   constexpr int N = 16, NRW = CPW / 8, NSV = CPW / 16, NVW = 8, SPL = N / NVW;
-  constexpr int G = CPW / 4;        // 4-channel groups
-  constexpr int NV = 64 * NSV;      // service threads
-  constexpr int IPT = T * G / NV;   // (step, channel group) items per service thread
-  constexpr int BPT = T * N / NV;   // B and C values per service thread
-  static_assert((CPW == 64 || CPW == 32) && SPL % 2 == 0, "B/C in float4 pieces");
-  static_assert(IPT >= 1 && BPT >= 1 && kChunkLen % T == 0, "sub-chunks tile the chunk");
+  constexpr int G = CPW / 4;                  // 4-channel groups
+  constexpr int NV = 64 * NSV;                // service threads
+  constexpr int IPT = T * G / NV;             // (step, channel group) items per service thread
+  constexpr int BPT = (T * N + NV - 1) / NV;  // B and C values per service thread (the last may repeat one)
+  static_assert((CPW == 64 || CPW == 80 || CPW == 32) && SPL % 2 == 0, "B/C in float4 pieces");
+  static_assert(IPT >= 1 && IPT * NV == T * G && kChunkLen % T == 0, "sub-chunks tile the chunk");
   using V = Vec4<IO>;
   typedef typename V::raw raw_t;
 
@@ -411,8 +413,8 @@ fwd_ws_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) float Y[2][T][NVW][CPW];       // per-lane partial sums
 
   if (w < NRW) {  // ------------------------------------------- recurrence waves
-    const int cl = lane % CPW;                   // channel in the tile
-    const int vw = w * (64 / CPW) + lane / CPW;  // state slice: states vw*SPL ..
+    const int cl = (w * 64 + lane) % CPW;  // channel in the tile
+    const int vw = (w * 64 + lane) / CPW;  // state slice: states vw*SPL ..
     const int64_t d = d0 + cl;
     const bool dv = d < D;
     const int64_t dc = dv ? d : D - 1;
@@ -542,7 +544,7 @@ fwd_ws_kernel(FwdArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
-      const int i = vt + j * NV;
+      const int i = BPT * NV > T * N ? (vt + j * NV) % (T * N) : vt + j * NV;  // past T*N: a repeat, not staged
       const int64_t t = k * T + i / N;
       const int64_t idx = mrow(t < Ls ? t : Ls - 1) * N + i % N;
       rb[j] = load_io(Bm, idx);
@@ -606,6 +608,7 @@ fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
       const int i = vt + j * NV;
+      if (BPT * NV > T * N && i >= T * N) continue;
       const int tl = i / N, n = i % N;
       BC[buf][tl][n / SPL][n % SPL] = rb[j];
       if (MODE == 0) BC[buf][tl][n / SPL][SPL + n % SPL] = rc[j];
@@ -693,9 +696,13 @@ constexpr int kWsSteps = 16, kWsRing = 2;
 template <typename IO, int CPW, int MODE, bool ZOH>
 static void launch_ws(const FwdArgs &a, dim3 grid, hipStream_t s) {
   const dim3 block(64 * (CPW / 8 + CPW / 16));
-  if (a.conv_k)
-    hipLaunchKernelGGL((fwd_ws_kernel<IO, CPW, kWsSteps, kWsRing, true, MODE, ZOH, true>), grid, block, 0, s, a);
-  else if (a.flags)
+  if constexpr (CPW != 80) {  // not instantiated on 80-channel tiles, which the launcher never gives it
+    if (a.conv_k) {
+      hipLaunchKernelGGL((fwd_ws_kernel<IO, CPW, kWsSteps, kWsRing, true, MODE, ZOH, true>), grid, block, 0, s, a);
+      return;
+    }
+  }
+  if (a.flags)
     hipLaunchKernelGGL((fwd_ws_kernel<IO, CPW, kWsSteps, kWsRing, true, MODE, ZOH, false>), grid, block, 0, s, a);
   else
     hipLaunchKernelGGL((fwd_ws_kernel<IO, CPW, kWsSteps, kWsRing, false, MODE, ZOH, false>), grid, block, 0, s, a);
@@ -737,10 +744,12 @@ static int64_t split_len(int64_t B, int64_t L, int64_t D) {
 }
 
 // Channels per workgroup (CPW) for dstate N.  A 64-channel tile takes a CU
-// (84 KB of LDS); 32-channel tiles fit two (16 states) or three (fwd_kernel)
-// per CU.  Measured on MI355X: 64-channel tiles are fastest while the grid
-// fits in one round over the CUs; beyond that, 32-channel tiles avoid a
-// mostly idle second round.  SSM_FWD_CPW overrides the choice (tuning only).
+// (84 KB of LDS), an 80-channel one too (104 KB); 32-channel tiles fit two
+// (16 states) or three (fwd_kernel) per CU.  Measured on MI355X: 64-channel
+// tiles are fastest while the grid fits in one round over the CUs; beyond
+// that, 80-channel tiles (16 states) if they fit in one round, else 32-channel
+// tiles, avoid a mostly idle second round.  SSM_FWD_CPW overrides the choice
+// (tuning only).
 static int device_cus() {
   static int cus = [] {
     int dev = 0, n = 0;
@@ -760,11 +769,16 @@ static int pick_cpw(const FwdArgs &a) {
   }();
   constexpr int NPL = N >= 2 ? 2 : 1;
   constexpr int mincpw = 64 * NPL / N > 16 ? 64 * NPL / N : 16;
-  if (env == 16 || env == 32 || env == 64) return env < mincpw ? mincpw : env;
+  if (env == 16 || env == 32 || env == 64 || (N == 16 && env == 80)) return env < mincpw ? mincpw : env;
   if (mincpw > 32) return 64;
   if (split_len(a.B, a.L, a.D)) return 32;  // split sequences use 32-channel tiles
   const int64_t wg64 = a.B * ((a.D + 63) / 64);
-  return wg64 <= device_cus() ? 64 : 32;
+  if (wg64 <= device_cus()) return 64;
+  // 80-channel tiles (16 states only) where they fit in one round over the
+  // CUs and 64-channel tiles do not: one workgroup per CU does 1.25 times the
+  // work, instead of a second round for the tiles left over
+  if (N == 16 && a.B * ((a.D + 79) / 80) <= device_cus()) return 80;
+  return 32;
 }
 
 template <typename IO, int N, int CPW, bool ZOH, bool FLAGS>
@@ -821,9 +835,14 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
     // wave-specialised kernel, also for the options it implements
     if (split_len(a.B, a.L, a.D) == 0) {
       const bool zoh = (a.flags & kFlagZoh) != 0;
-      if (pick_cpw<N>(a) == 64) {
+      int cpw = pick_cpw<N>(a);
+      if (cpw == 80 && a.conv_k) cpw = 32;  // the convolution variant needs more than 128 registers
+      if (cpw == 64) {
         const dim3 grid((unsigned)((a.D + 63) / 64), (unsigned)a.B, 1);
         zoh ? launch_ws<IO, 64, 0, true>(a, grid, s) : launch_ws<IO, 64, 0, false>(a, grid, s);
+      } else if (cpw == 80) {
+        const dim3 grid((unsigned)((a.D + 79) / 80), (unsigned)a.B, 1);
+        zoh ? launch_ws<IO, 80, 0, true>(a, grid, s) : launch_ws<IO, 80, 0, false>(a, grid, s);
       } else {  // 32-channel tiles: several workgroups per CU
         const dim3 grid((unsigned)((a.D + 31) / 32), (unsigned)a.B, 1);
         zoh ? launch_ws<IO, 32, 0, true>(a, grid, s) : launch_ws<IO, 32, 0, false>(a, grid, s);

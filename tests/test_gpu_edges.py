@@ -56,6 +56,26 @@ def test_many_channel_tiles(ssm, dtype, opts):
     _check_fwd_opts(ssm, p, TOL[dtype], opts.get("zoh", False), opts.get("reverse", False))
 
 
+@pytest.mark.parametrize("opts", [dict(), dict(zoh=True), dict(reverse=True, tok=True)],
+                         ids=["plain", "zoh", "reverse-per-token"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_eighty_channel_tiles(ssm, dtype, opts):
+    """20480 channels in one row: 320 tiles of 64 channels would need a second
+    round over 256 compute units, 256 tiles of 80 need one, so the 16-state
+    forward takes 80-channel tiles there (on a 256-CU device)."""
+    from tests.test_gpu_options import _check_fwd as _check_fwd_opts, _with_opts
+    p = _with_opts(_problem(1, 37, 20480, 16, dtype, seed=43, h0=True), opts.get("tok", False))
+    _check_fwd_opts(ssm, p, TOL[dtype], opts.get("zoh", False), opts.get("reverse", False))
+
+
+@pytest.mark.parametrize("z,Dskip", [(True, True), (False, False)], ids=["gated", "no-gate-no-skip"])
+def test_eighty_channel_tiles_ragged(ssm, z, Dskip):
+    """16408 channels: 257 tiles of 64, 206 tiles of 80 of which the last holds
+    8 channels."""
+    p = _problem(1, 20, 16408, 16, torch.float32, seed=44, z=z, Dskip=Dskip, h0=True)
+    _check_fwd(ssm, p, 1e-4)
+
+
 def test_nan_propagates_in_its_channel_only(ssm):
     """A NaN input poisons its own channel from that step on (through the
     state) and nothing else: channels are independent recurrences."""

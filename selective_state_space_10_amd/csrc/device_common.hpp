@@ -38,6 +38,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ float load_io(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float load_io(const bf16* p, int64_t i) { return bf16_bits_to_f32(p[i].bits); }
+// the IO type stored at a byte offset from a base
+template <typename IO>
+__device__ __forceinline__ float load_io_b(const char* p, uint32_t o) { return load_io(reinterpret_cast<const IO*>(p + o), 0); }
 __device__ __forceinline__ void store_io(float* p, int64_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void store_io(bf16* p, int64_t i, float v) { p[i].bits = f32_to_bf16_bits(v); }
 
@@ -49,6 +52,13 @@ template <>
 struct Vec4<float> {
   typedef float4 raw;
   static __device__ __forceinline__ raw load(const float *p, int64_t i) { return *(const float4 *)(p + i); }
+  // at a byte offset from a base
+  static __device__ __forceinline__ raw load_b(const char *p, uint32_t o) { return *(const float4 *)(p + o); }
+  static __device__ __forceinline__ void store_b(char *p, uint32_t o, float4 v) { *(float4 *)(p + o) = v; }
+  static __device__ __forceinline__ raw splat_b(const char *p, uint32_t o) {
+    const float v = *(const float *)(p + o);
+    return make_float4(v, v, v, v);
+  }
   static __device__ __forceinline__ float4 cvt(raw r) { return r; }
   static __device__ __forceinline__ void store(float *p, int64_t i, float4 v) { *(float4 *)(p + i) = v; }
   // one element, repeated four times
@@ -61,6 +71,13 @@ template <>
 struct Vec4<bf16> {
   typedef uint2 raw;
   static __device__ __forceinline__ raw load(const bf16 *p, int64_t i) { return *(const uint2 *)(p + i); }
+  static __device__ __forceinline__ raw load_b(const char *p, uint32_t o) { return *(const uint2 *)(p + o); }
+  static __device__ __forceinline__ void store_b(char *p, uint32_t o, float4 v) { store(reinterpret_cast<bf16 *>(p + o), 0, v); }
+  static __device__ __forceinline__ raw splat_b(const char *p, uint32_t o) {
+    const uint32_t b = *(const uint16_t *)(p + o);
+    const uint32_t w = b | (b << 16);
+    return make_uint2(w, w);
+  }
   static __device__ __forceinline__ float4 cvt(raw r) {
     return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
                        __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));

@@ -500,6 +500,39 @@ fwd_ws_kernel(FwdArgs a) {
   auto mrow = [&](int64_t t) {  // memory row of segment step t
     return row0 + (rev ? L - 1 - (tb + t) : tb + t);
   };
+  // Addresses: 32-bit byte offsets from the segment's first row in memory (a
+  // uniform base), advanced by one sub-chunk per iteration and clamped to the
+  // segment's rows by one med3 (steps past the end read the last step).  The
+  // launcher keeps (segment length + 64) rows of a (B,L,D) array below 2^31
+  // bytes.
+  constexpr int SZ = (int)sizeof(IO);
+  const int64_t lo = rev ? row0 + L - tb - Ls : row0 + tb;  // lowest memory row of the segment
+  const int DS = (int)D * SZ, NS = N * SZ;                   // bytes per row: (B,L,D) and (B,L,N) arrays
+  const int kstep = (rev ? -T : T) * DS, kstep_bc = (rev ? -T : T) * NS, kstep_tok = (rev ? -T : T) * SZ;
+  const char *__restrict__ u_b = (const char *)(u + lo * D);
+  const char *__restrict__ dl_b = (const char *)(dl + lo * D);
+  const char *__restrict__ dlt_b = (const char *)(dl + lo);  // one step size per token: (B,L)
+  const char *__restrict__ B_b = (const char *)(Bm + lo * N);
+  const char *__restrict__ C_b = (const char *)(Cm + lo * N);
+  const char *__restrict__ z_b = (const char *)(zsrc + lo * D);
+  char *__restrict__ y_b = (char *)(y + lo * D);
+  auto seg_row = [&](int t) { return rev ? (int)Ls - 1 - t : t; };  // row of sub-chunk-0 step t from lo
+  int o_it[IPT], o_tok[IPT], o_bc[BPT];  // offsets at sub-chunk 0, before clamping
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    o_it[j] = seg_row(tl0 + j * (NV / G)) * DS + (int)dgc * SZ;
+    o_tok[j] = seg_row(tl0 + j * (NV / G)) * SZ;
+  }
+  const int it_lo = (int)dgc * SZ, it_hi = ((int)Ls - 1) * DS + (int)dgc * SZ, tok_hi = ((int)Ls - 1) * SZ;
+  int bc_lo[BPT], bc_hi[BPT];
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int i = BPT * NV > T * N ? (vt + j * NV) % (T * N) : vt + j * NV;  // past T*N: a repeat, not staged
+    o_bc[j] = seg_row(i / N) * NS + (i % N) * SZ;
+    bc_lo[j] = (i % N) * SZ;
+    bc_hi[j] = ((int)Ls - 1) * NS + (i % N) * SZ;
+  }
+  auto clampi = [](int v, int lo_, int hi_) { return min(max(v, lo_), hi_); };  // one v_med3_i32
   float bias4[4] = {0.f, 0.f, 0.f, 0.f}, Dsk4[4] = {0.f, 0.f, 0.f, 0.f};
   float cw[4][XK], cb4[4] = {0.f, 0.f, 0.f, 0.f};  // convolution taps (zero past the width) and bias
 #pragma unroll
@@ -522,15 +555,20 @@ fwd_ws_kernel(FwdArgs a) {
   float r_b[R][BPT], r_c[R][BPT];
   float4 keep_du[2][IPT], keep_g[2][IPT];         // D*u and silu(z), by sub-chunk parity
 
-  auto load_chunk = [&](int64_t k, raw_t(&ra)[IPT], raw_t(&ru)[IPT], raw_t(&rz)[IPT], float(&rb)[BPT],
+  // Loads of sub-chunk k; `zero` (always 0) only orders them after its producer.
+  auto load_chunk = [&](int64_t k, int zero, raw_t(&ra)[IPT], raw_t(&ru)[IPT], raw_t(&rz)[IPT], float(&rb)[BPT],
                         float(&rc)[BPT], raw_t(&rx)[IPT][XK]) {
+    const int kk32 = (int)k;
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
-      const int64_t t = k * T + tl0 + j * (NV / G);
-      const int64_t r = mrow(t < Ls ? t : Ls - 1);
-      const int64_t idx = r * D + dgc;
-      ra[j] = tok ? V::splat(dl, r) : V::load(dl, idx);
+      const uint32_t o = (uint32_t)clampi(o_it[j] + zero + kk32 * kstep, it_lo, it_hi);
+      if (FLAGS && tok)
+        ra[j] = V::splat_b(dlt_b, (uint32_t)clampi(o_tok[j] + zero + kk32 * kstep_tok, 0, tok_hi));
+      else
+        ra[j] = V::load_b(dl_b, o);
       if (CONV) {  // rows r-(K-1) .. r, clamped into the sequence (rows before 0 are zeroed later)
+        const int64_t t = k * T + tl0 + j * (NV / G) + zero;
+        const int64_t r = mrow(t < Ls ? t : Ls - 1);
 #pragma unroll
         for (int kk = 0; kk < XK; ++kk) {
           int64_t ts = r - row0 - (ck - 1) + kk;
@@ -538,17 +576,15 @@ fwd_ws_kernel(FwdArgs a) {
           rx[j][kk] = V::load(xin, (row0 + ts) * D + dgc);
         }
       } else {
-        ru[j] = V::load(u, idx);
+        ru[j] = V::load_b(u_b, o);
       }
-      if (MODE == 0) rz[j] = V::load(zsrc, idx);
+      if (MODE == 0) rz[j] = V::load_b(z_b, o);
     }
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
-      const int i = BPT * NV > T * N ? (vt + j * NV) % (T * N) : vt + j * NV;  // past T*N: a repeat, not staged
-      const int64_t t = k * T + i / N;
-      const int64_t idx = mrow(t < Ls ? t : Ls - 1) * N + i % N;
-      rb[j] = load_io(Bm, idx);
-      if (MODE == 0) rc[j] = load_io(Cm, idx);
+      const uint32_t o = (uint32_t)clampi(o_bc[j] + zero + kk32 * kstep_bc, bc_lo[j], bc_hi[j]);
+      rb[j] = load_io_b<IO>(B_b, o);
+      if (MODE == 0) rc[j] = load_io_b<IO>(C_b, o);
     }
   };
   auto prologue = [&](int64_t k, raw_t(&ra)[IPT], raw_t(&ru)[IPT], raw_t(&rz)[IPT], float(&rb)[BPT],
@@ -557,7 +593,7 @@ fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int tl = tl0 + j * (NV / G);
-      const bool tv = k * T + tl < Ls;  // steps past the end get dt = 0: no state change
+      const bool tv = (int)k * T + tl < (int)Ls;  // steps past the end get dt = 0: no state change
       const float4 r = V::cvt(ra[j]);
       float4 x;
       if (CONV) {  // u = silu(bias + sum_k w_k x[t - (K-1) + k]), x = 0 before the first row
@@ -619,8 +655,7 @@ fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
       const int tl = tl0 + j * (NV / G);
-      const int64_t t = k * T + tl;
-      if (t < Ls && gv) {
+      if ((int)k * T + tl < (int)Ls && gv) {
         float4 s = *(const float4 *)&Y[buf][tl][0][4 * g];
 #pragma unroll
         for (int ww = 1; ww < NVW; ++ww) {
@@ -631,12 +666,12 @@ fwd_ws_kernel(FwdArgs a) {
         s.y = (s.y + kdu[j].y) * kg[j].y;
         s.z = (s.z + kdu[j].z) * kg[j].z;
         s.w = (s.w + kdu[j].w) * kg[j].w;
-        const int64_t yi = mrow(t) * D + dg;
+        const uint32_t yo = (uint32_t)(o_it[j] + (int)k * kstep);  // t < Ls: no clamp
         if (accum) {
-          const float4 o = V::cvt(V::load(y, yi));
+          const float4 o = V::cvt(V::load_b(y_b, yo));
           s.x += o.x, s.y += o.y, s.z += o.z, s.w += o.w;
         }
-        V::store(y, yi, s);
+        V::store_b(y_b, yo, s);
       }
     }
   };
@@ -646,9 +681,9 @@ fwd_ws_kernel(FwdArgs a) {
   // unconditionally: a register slot that is only sometimes refilled would
   // make the compiler copy it and wait for loads still in flight.
 #pragma unroll
-  for (int j = 0; j < R; ++j) load_chunk(j, r_dl[j], r_u[j], r_z[j], r_b[j], r_c[j], r_x[j]);
+  for (int j = 0; j < R; ++j) load_chunk(j, 0, r_dl[j], r_u[j], r_z[j], r_b[j], r_c[j], r_x[j]);
   prologue(0, r_dl[0], r_u[0], r_z[0], r_b[0], r_c[0], r_x[0], keep_du[0], keep_g[0]);
-  load_chunk(R, r_dl[0], r_u[0], r_z[0], r_b[0], r_c[0], r_x[0]);
+  load_chunk(R, 0, r_dl[0], r_u[0], r_z[0], r_b[0], r_c[0], r_x[0]);
   __syncthreads();  // sub-chunk 0 staged
   // Iteration k (the recurrence waves scan sub-chunk k): epilogue of k-1,
   // then prologue of k+1 and the loads of k+1+R into the slot it frees.
@@ -668,7 +703,7 @@ fwd_ws_kernel(FwdArgs a) {
       zero = after_all(zero, r_dl[rs], r_x[rs], r_b[rs]);
     else
       zero = after_all(zero, r_dl[rs], r_u[rs], r_b[rs]);
-    load_chunk(k + 1 + R + zero, r_dl[rs], r_u[rs], r_z[rs], r_b[rs], r_c[rs], r_x[rs]);
+    load_chunk(k + 1 + R, zero, r_dl[rs], r_u[rs], r_z[rs], r_b[rs], r_c[rs], r_x[rs]);
     __syncthreads();
   };
   int64_t k = 0;
@@ -731,7 +766,12 @@ __global__ void __launch_bounds__(256) fwd_seg_combine_kernel(FwdArgs a, int64_t
 constexpr int64_t kMinSeg = 4096;
 constexpr int64_t kSplitTarget = 512;
 
-static int64_t split_len(int64_t B, int64_t L, int64_t D) {
+// The wave-specialised kernel addresses a segment with 32-bit byte offsets:
+// (segment length + 64) rows of a (B,L,D) array must stay below 2^31 bytes.
+static int64_t ws_max_rows(int64_t D, int64_t io_bytes) { return ((int64_t)1 << 31) / (D * io_bytes) - 64; }
+
+// Segment length of a sequence split (0: no split), io_bytes per element.
+static int64_t split_len(int64_t B, int64_t L, int64_t D, int64_t io_bytes) {
   const int64_t tiles64 = B * ((D + 63) / 64);
   if (tiles64 >= 128 || L < 2 * kMinSeg) return 0;
   const int64_t tiles32 = B * ((D + 31) / 32);
@@ -740,7 +780,10 @@ static int64_t split_len(int64_t B, int64_t L, int64_t D) {
   if (nseg < 2) return 0;
   int64_t len = (L + nseg - 1) / nseg;
   len = (len + kChunkLen - 1) / kChunkLen * kChunkLen;
-  return len;
+  // more, shorter segments where a segment would not fit 32-bit offsets
+  // (D < 8192 here, so the cap is at least 65472 steps)
+  const int64_t cap = ws_max_rows(D, io_bytes) / kChunkLen * kChunkLen;
+  return len < cap ? len : cap;
 }
 
 // Channels per workgroup (CPW) for dstate N.  A 64-channel tile takes a CU
@@ -771,7 +814,7 @@ static int pick_cpw(const FwdArgs &a) {
   constexpr int mincpw = 64 * NPL / N > 16 ? 64 * NPL / N : 16;
   if (env == 16 || env == 32 || env == 64 || (N == 16 && env == 80)) return env < mincpw ? mincpw : env;
   if (mincpw > 32) return 64;
-  if (split_len(a.B, a.L, a.D)) return 32;  // split sequences use 32-channel tiles
+  if (split_len(a.B, a.L, a.D, 4)) return 32;  // split sequences use 32-channel tiles (the io size only caps the length)
   const int64_t wg64 = a.B * ((a.D + 63) / 64);
   if (wg64 <= device_cus()) return 64;
   // 80-channel tiles (16 states only) where they fit in one round over the
@@ -789,7 +832,7 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   constexpr int IPT = T * (CPW / 4) / (64 * NW);
   constexpr int PD = IPT <= 2 ? 2 : 1;
   FwdArgs a = a0;
-  a.seg_len = split_len(a.B, a.L, a.D);
+  a.seg_len = split_len(a.B, a.L, a.D, sizeof(IO));
   const unsigned tiles = (unsigned)((a.D + CPW - 1) / CPW);
   if (a.seg_len == 0) {
     hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0, ZOH, FLAGS>), dim3(tiles, (unsigned)a.B, 1), dim3(64 * NW), 0, s,
@@ -833,7 +876,8 @@ static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
   if constexpr (N == 16) {
     // 64-channel tiles in one round over the CUs and no sequence split: the
     // wave-specialised kernel, also for the options it implements
-    if (split_len(a.B, a.L, a.D) == 0) {
+    // (unless a row of an array spans 2^31 bytes: then fwd_kernel, 64-bit offsets)
+    if (split_len(a.B, a.L, a.D, sizeof(IO)) == 0 && a.L <= ws_max_rows(a.D, sizeof(IO))) {
       const bool zoh = (a.flags & kFlagZoh) != 0;
       int cpw = pick_cpw<N>(a);
       if (cpw == 80 && a.conv_k) cpw = 32;  // the convolution variant needs more than 128 registers
@@ -874,8 +918,8 @@ static hipError_t launch_fwd_io(const FwdArgs &a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-int64_t fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int) {
-  const int64_t len = split_len(B, L, D);
+int64_t fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype) {
+  const int64_t len = split_len(B, L, D, io_dtype == 0 ? 4 : 2);
   if (len == 0) return 0;
   const int64_t nseg = (L + len - 1) / len;
   return (2 * B * nseg * D * N + B * nseg * D) * 4;

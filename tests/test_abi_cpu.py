@@ -62,6 +62,28 @@ def test_version_and_queries(lib):
     assert lib.ssm_status_string(99) == b"unknown status"
 
 
+@pytest.mark.parametrize("L,D,io,nseg_uncapped", [(1 << 20, 1024, 0, 16), (1 << 22, 4096, 0, 4),
+                                                  (1 << 22, 4096, 1, 4)])
+def test_fwd_split_segments_fit_32bit_offsets(lib, L, D, io, nseg_uncapped):
+    """A split sequence's segments are what the forward workspace holds
+    (per segment: two (D,N) state arrays and a D-vector of step-size sums). The
+    forward kernel addresses a segment with 32-bit byte offsets, so a segment
+    of a (B,L,D) array, plus 64 rows of slack, stays below 2^31 bytes: long
+    segments are cut into more."""
+    N, sz = 16, (4, 2)[io]
+    wsb = lib.ssm_scan_fwd_workspace_bytes(1, L, D, N, io)
+    nseg, rem = divmod(wsb, 4 * D * (2 * N + 1))
+    assert wsb > 0 and rem == 0
+    seg = -(-L // nseg)
+    seg = -(-seg // 32) * 32
+    fits = (seg + 64) * D * sz < 1 << 31
+    assert fits
+    if (-(-L // nseg_uncapped) + 64) * D * sz < 1 << 31:
+        assert nseg == nseg_uncapped
+    else:
+        assert nseg > nseg_uncapped
+
+
 def _fwd(lib, B=1, L=16, D=8, N=4, io=0, **kw):
     p = dict(u=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE, Dskip=None, z=None, bias=None,
              h0=None, hf=None, y=FAKE, cs=None, ws=None)

@@ -190,6 +190,29 @@ def test_fwd_workload4_full_size(ssm):
     _sampled_fwd(ssm, 4, 4)
 
 
+@pytest.mark.parametrize("reverse", [False, True], ids=["forward", "reverse"])
+@pytest.mark.parametrize("L", [65472, 65536])
+def test_fwd_rows_near_2gib(ssm, L, reverse):
+    """8192 fp32 channels: 65472 steps are the most the 16-state kernel
+    addresses with 32-bit offsets (its largest offsets, just under 2^31); at
+    65536 a batch row of each (B,L,D) array spans 2 GiB and the forward takes
+    the all-purpose kernel with 64-bit offsets. Sampled channels against the
+    oracle."""
+    from tests.test_gpu_options import _fwd as _fwd_opts
+    D = 8192
+    p = scan_inputs(1, L, D, 16, torch.float32, seed=12, device="cuda")
+    y, hf, _ = _fwd_opts(ssm, p, reverse=reverse, return_final_state=True)
+    torch.cuda.synchronize()
+    sel = torch.tensor([0, 1, 2, 3, 4100, 4101, 4102, 4103, D - 4, D - 3, D - 2, D - 1])
+    ps = _slice_channels(p, sel.cuda())
+    y_s, hf_s = y[:, :, sel.cuda()].cpu(), hf[:, sel.cuda()].cpu()
+    del p, y, hf
+    torch.cuda.empty_cache()
+    yo, hfo, _ = oracle_c.scan_fwd(**_oracle_kwargs(ps), reverse=reverse)
+    assert nmax_err(y_s, yo) <= 1e-4
+    assert nmax_err(hf_s, hfo) <= 1e-4
+
+
 def test_fwd_deterministic_and_stream(ssm):
     p = _to(_problem(2, 400, 136, 16, torch.float32, seed=3, h0=True), "cuda")
     y1, h1, c1 = _gpu_fwd(ssm, p, return_final_state=True, save_chunk_states=True)

@@ -31,6 +31,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+# Vector-ALU rates of MI355X: the published fp32 vector peak, 157.3 TFLOP/s, is
+# 78.6e12 FP32 lane operations/s (an FMA counts two flops); exp2, log2 and rcp
+# run at a quarter of that rate (measured on gfx950: about 8.4 SIMD cycles per
+# wave64 v_exp_f32 against about 2 for a plain FP32 operation).
+VALU_OPS_PER_S = 157.3e12 / 2
+TRANS_OPS_PER_S = VALU_OPS_PER_S / 4
 WORKLOAD_NAMES = ["mamba-370m-layer-fwd", "mamba-2.8b-layer-fwd", "decode-state-update",
                   "million-length-fwd", "million-length-bwd", "mamba-370m-layer-bwd",
                   "mamba-370m-layer-fwd-zoh", "mamba-370m-layer-fwd-token-delta",
@@ -242,6 +248,8 @@ def bench_fwd(args, idx, name, zoh=False, per_token=False, bidirectional=False, 
     if bidirectional:
         line["roofline"]["note"] = ("two launches per step; algorithmic bytes are one read of "
                                     "the inputs and one write of y")
+    if not (zoh or per_token or bidirectional or conv):
+        line["roofline"]["alu"] = _alu_floor(Bsz, L, D, N, ms_launch)
     if not (per_token or conv):
         ceil = _r3w1_ceiling(sets, max(args.steps, 10))
         ceil["frac"] = achieved / ceil["achieved"]  # the scan's rate over the measured ceiling
@@ -251,6 +259,24 @@ def bench_fwd(args, idx, name, zoh=False, per_token=False, bidirectional=False, 
         pc = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in pc.items()}
         line["cpu_baseline"] = _cpu_baseline_fwd(pc)
     return line
+
+
+def _alu_floor(Bsz, L, D, N, ms_launch):
+    """The forward's vector-ALU floor: per state update 4 FP32 operations
+    (dt*A', dt*u*B, the state FMA, the C*h FMA) and one exp2; per (b,t,d), shared
+    by the N states, 10 FP32 operations (step size and softplus 4, SiLU 2, dt*u,
+    D*u, the skip add, the gate) and 4 transcendentals (softplus: exp2, log2;
+    SiLU: exp2, rcp)."""
+    upd, td = Bsz * L * D * N, Bsz * L * D
+    floor_s = (upd * (4 / VALU_OPS_PER_S + 1 / TRANS_OPS_PER_S)
+               + td * (10 / VALU_OPS_PER_S + 4 / TRANS_OPS_PER_S))
+    achieved = upd / (ms_launch * 1e-3) / 1e9
+    peak = upd / floor_s / 1e9
+    return {"kind": "vector-ALU floor of the plain forward (4 FP32 ops + 1 exp2 per state update, "
+                    "10 FP32 ops + 4 transcendentals per (b,t,d)) at the published fp32 vector rate, "
+                    "transcendentals at a quarter of it",
+            "achieved": achieved, "peak": peak, "unit": "Gupdates/s", "frac": achieved / peak,
+            "floor_ms": floor_s * 1e3}
 
 
 def bench_decode(args, zoh=False):

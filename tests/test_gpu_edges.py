@@ -32,6 +32,17 @@ def test_lengths_around_the_chunk(ssm, L):
     _check_bwd(ssm, p, 1e-4, seed=L)
 
 
+@pytest.mark.parametrize("L", [1, 2, 15, 16, 17, 31, 33, 49])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_reverse_lengths_around_the_chunk(ssm, L, dtype):
+    """The reverse direction with one step size per token at lengths below,
+    at and above a 16-step sub-chunk: loads of steps past the end are clamped
+    to the segment's first row in memory."""
+    from tests.test_gpu_options import _check_fwd as _check_fwd_opts, _with_opts
+    p = _with_opts(_problem(2, L, 72, 16, dtype, seed=100 + L, h0=True), True)
+    _check_fwd_opts(ssm, p, TOL[dtype], reverse=True)
+
+
 @pytest.mark.parametrize("B,L,D,N,dtype", [(1, 40, 8, 16, torch.float32),
                                            (5, 33, 8, 4, torch.bfloat16),
                                            (64, 7, 64, 16, torch.float32),

@@ -215,3 +215,12 @@ def test_header_compiles_as_c_and_cpp(tmp_path):
         r = subprocess.run(["gcc", *lang, "-Wall", "-Werror", "-fsyntax-only", "-I", inc, str(src)],
                            capture_output=True, text=True)
         assert r.returncode == 0, r.stderr
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No fallback: without the built HIP library the loader raises."""
+    import selective_state_space_10_amd._lib as L
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", os.path.join(ROOT, "no-such-dir", "libssm_scan.so"))
+    with pytest.raises(ImportError, match="not built"):
+        L.load()

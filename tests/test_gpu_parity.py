@@ -278,6 +278,35 @@ def test_decode_workload3_full_size(ssm):
     _decode_check(ssm, d, w.steps, TOL[w.io_dtype], sel=sel)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_decode_unaligned_token_b_c(ssm, dtype):
+    """B and C only aligned to their element, which the state update allows:
+    the same result as the aligned call, and the oracle's."""
+    def misalign(x):
+        buf = torch.empty(x.numel() + 1, dtype=x.dtype, device=x.device)
+        buf[1:].copy_(x.reshape(-1))
+        return buf[1:].view(x.shape)
+
+    d = decode_inputs(3, 72, 16, 2, dtype, seed=21)
+    dg = _to(d, "cuda")
+    st_a, st_u = dg["state"].clone(), dg["state"].clone()
+    so = d["state"]
+    for t in range(2):
+        Bu, Cu = misalign(dg["B"][t]), misalign(dg["C"][t])
+        assert Bu.data_ptr() % (4 * Bu.element_size()) != 0
+        args = (dg["u"][t], dg["delta"][t], dg["A"])
+        rest = (dg["D"], dg["z"][t], dg["delta_bias"], True)
+        ya = ssm.state_update(st_a, *args, dg["B"][t], dg["C"][t], *rest)
+        yu = ssm.state_update(st_u, *args, Bu, Cu, *rest)
+        so, yo = oracle_c.state_update(so, d["u"][t], d["delta"][t], d["A"], d["B"][t], d["C"][t],
+                                       d["D"], d["z"][t], d["delta_bias"], True)
+        torch.cuda.synchronize()
+        assert torch.equal(ya, yu)
+        assert nmax_err(yu, yo) <= TOL[dtype]
+    assert torch.equal(st_a, st_u)
+    assert nmax_err(st_u, so) <= TOL[dtype]
+
+
 def test_decode_matches_scan_on_gpu(ssm):
     """64 single-token updates equal one 64-step scan (both on the GPU)."""
     p = _to(_problem(2, 64, 72, 16, torch.float32, seed=12, h0=True), "cuda")

@@ -40,6 +40,8 @@ namespace {
 
 constexpr int kCPW = 64;  // channels per workgroup (one per lane)
 constexpr int kTE = 8;    // steps per epilogue group
+constexpr int kXStride = 36;  // floats per channel-sum staging plane (32 values + padding)
+constexpr int kXRot = 12;     // rotation of the odd staging planes
 constexpr int kSwap1 = 0xB1;  // DPP quad_perm(1,0,3,2): value of lane ^ 1
 constexpr int kSwap2 = 0x4E;  // DPP quad_perm(2,3,0,1): value of lane ^ 2
 
@@ -192,9 +194,16 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
   __shared__ __attribute__((aligned(16))) float U[T][CPW];   // u
   __shared__ __attribute__((aligned(16))) float SG[T][CPW];  // d dt / d raw delta
   __shared__ __attribute__((aligned(16))) float GZ[T][CPW];  // dy * silu'(z)
-  __shared__ __attribute__((aligned(16))) float BCs[2][T][NW][4];  // B, C in the slot order of each lane parity
+  // B, C of (step, state slice) in the slot order of each lane parity; the
+  // second parity's plane is offset by 16 bytes, so that a wave's read of both
+  // planes (even and odd lanes) touches different banks
+  __shared__ __attribute__((aligned(16))) float BCs[2][T * NW * 4 + 4];
+  auto bcs = [&](int pp, int tl, int sl) { return &BCs[pp][(tl * NW + sl) * 4]; };
   __shared__ __attribute__((aligned(16))) float Q[3][TE][NW][64];  // per-lane partials: C h, lambda B, r A
-  __shared__ __attribute__((aligned(16))) float X[NW][TE][4][32];  // channel-sum staging of dB, dC
+  // Channel-sum staging of dB, dC: 32 values per plane, planes padded to 36
+  // floats and odd planes rotated by 12 places, so that both the per-step
+  // stores and the channel sums' 16-byte reads are free of bank conflicts.
+  __shared__ __attribute__((aligned(16))) float X[NW][TE][4][kXStride];
 
   // --- prologue ownership: channel group g, steps tl0 + j*(NT/G)
   const int g = tid % G;
@@ -364,8 +373,8 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
         const float bv = MODE == 0 ? r_b[j] : 0.0f;
 #pragma unroll
         for (int pp = 0; pp < NPL; ++pp) {
-          BCs[pp][tl][sl][k ^ pp] = bv;
-          BCs[pp][tl][sl][NPL + (k ^ pp)] = r_c[j];
+          bcs(pp, tl, sl)[k ^ pp] = bv;
+          bcs(pp, tl, sl)[NPL + (k ^ pp)] = r_c[j];
         }
       }
     }
@@ -382,7 +391,7 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
       for (int tl = T - 1; tl >= 0; --tl) {
         const float dt = P[tl][lane].x;
         const float e = E[tl][lane];
-        const float4 bc = *(const float4 *)&BCs[par][tl][w][0];
+        const float4 bc = *(const float4 *)bcs(par, tl, w);
         const float cv[2] = {NPL == 2 ? bc.z : bc.y, bc.w};
 #pragma unroll
         for (int s = 0; s < NPL; ++s) {
@@ -439,7 +448,8 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
     }
   };
   // dB, dC over this workgroup's channels: lane (o = lane/2, half = lane%2)
-  // adds 16 staged values of output o, then its partner's 16.
+  // adds 16 staged values of output o, then its partner's 16 (the rotation of
+  // odd planes only changes which lane of the pair adds which values).
   auto channel_sums = [&](int64_t kc, int tg) {
     const int64_t t0 = tb + kc * T;
     const int o = lane >> 1, half = lane & 1;
@@ -476,7 +486,7 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
 #pragma unroll
       for (int tl = 0; tl < T; ++tl) {
         const float2 p = P[tl][lane];
-        const float4 bc = *(const float4 *)&BCs[par][tl][w][0];
+        const float4 bc = *(const float4 *)bcs(par, tl, w);
         const float bv[2] = {bc.x, bc.y};
 #pragma unroll
         for (int s = 0; s < NPL; ++s) {
@@ -496,7 +506,7 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
         const int tl = tg * TE + tq;
         const float2 p = P[tl][lane];
         const float e = E[tl][lane];
-        const float4 bc = *(const float4 *)&BCs[par][tl][w][0];
+        const float4 bc = *(const float4 *)bcs(par, tl, w);
         const float bv[2] = {bc.x, bc.y};
         const float cv[2] = {NPL == 2 ? bc.z : bc.y, bc.w};
         float pre = 0.0f, dup = 0.0f, ddp = 0.0f, cB[NPL], cC[NPL];
@@ -530,11 +540,13 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
         Q[1][tq][w][lane] = dup;
         Q[2][tq][w][lane] = ddp;
         if constexpr (NPL == 2) {
-          X[w][tq][par][lane >> 1] = cB[0] + dpp_mov<kSwap1>(cB[1]);
-          X[w][tq][2 + par][lane >> 1] = cC[0] + dpp_mov<kSwap1>(cC[1]);
+          const int xi = ((lane >> 1) + kXRot * par) & 31;
+          X[w][tq][par][xi] = cB[0] + dpp_mov<kSwap1>(cB[1]);
+          X[w][tq][2 + par][xi] = cC[0] + dpp_mov<kSwap1>(cC[1]);
         } else {
-          X[w][tq][lane >> 5][lane & 31] = cB[0];
-          X[w][tq][2 + (lane >> 5)][lane & 31] = cC[0];
+          const int xi = ((lane & 31) + kXRot * (lane >> 5)) & 31;
+          X[w][tq][lane >> 5][xi] = cB[0];
+          X[w][tq][2 + (lane >> 5)][xi] = cC[0];
         }
       }
       __syncthreads();

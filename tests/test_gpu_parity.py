@@ -270,6 +270,14 @@ def test_decode_no_optionals(ssm):
     _decode_check(ssm, d, 3, TOL[torch.float32])
 
 
+@pytest.mark.parametrize("N", [4, 16])
+def test_decode_more_rows_than_one_grid(ssm, N):
+    """More batch rows than one launch's grid holds (65535): the rows past it
+    go to further launches with a row offset."""
+    d = decode_inputs(65537, 8, N, 2, torch.bfloat16, seed=33)
+    _decode_check(ssm, d, 2, TOL[torch.bfloat16])
+
+
 def test_decode_workload3_full_size(ssm):
     w = WORKLOADS[3]
     d = decode_inputs(w.batch, w.dim, w.dstate, w.steps, w.io_dtype, seed=3)

@@ -421,6 +421,38 @@ def test_bwd_workload4_full_size(ssm):
         assert nmax_err(gr[k][sc], go[k]) <= tol, k
 
 
+def test_bwd_workload1_shape_full_size(ssm):
+    """Backward at the Mamba-370m layer shape (fp32, 8 batch rows, 32 channel
+    tiles, no sequence split), as the benchmark runs it.  The cotangent is zero
+    outside sampled channels in every tile position the staging of the channel
+    sums distinguishes (first and last of a tile, both lane parities), so the
+    oracle computes dB and dC over those channels; all gradients of the other
+    channels must be exactly zero."""
+    w = WORKLOADS[1]
+    p = workload_inputs(1, device="cuda")
+    y, hf, cs = _gpu_fwd(ssm, p, return_final_state=True, save_chunk_states=True)
+    sel = torch.tensor([0, 1, 62, 63, 64, 777, 1030, 1500, w.dim - 2, w.dim - 1])
+    mask = torch.zeros(w.dim, dtype=torch.bool)
+    mask[sel] = True
+    dy = cotangent(y, 1)
+    dy[:, :, ~mask.cuda()] = 0
+    gr = ssm.scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                      p["delta_bias"], True, None, cs, dy)
+    torch.cuda.synchronize()
+    ps = _slice_channels(dict(p, dy=dy), sel.cuda())
+    go = oracle_c.scan_bwd(**_oracle_kwargs(ps), dy=ps["dy"])
+    tol = TOL[w.io_dtype]
+    sc = sel.cuda()
+    for k in ("du", "ddelta", "dz"):
+        assert nmax_err(gr[k][:, :, sc], go[k]) <= tol, k
+        assert int(torch.count_nonzero(gr[k][:, :, ~mask.cuda()])) == 0, k
+    for k in ("dB", "dC"):
+        assert nmax_err(gr[k], go[k]) <= tol, k
+    for k in ("dA", "dD", "ddelta_bias"):
+        assert nmax_err(gr[k][sc], go[k]) <= tol, k
+        assert int(torch.count_nonzero(gr[k][~mask.cuda()])) == 0, k
+
+
 def test_autograd_function(ssm):
     p = _to(_problem(2, 150, 64, 16, torch.float32, seed=21, h0=True), "cuda")
     leaves = {k: p[k].clone().requires_grad_(True) for k in

@@ -604,6 +604,9 @@ __global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(BwdArgs a, BwdWs ws)
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
     const int64_t b = i / LN, r = i % LN;
     float sb = 0.0f, sc = 0.0f;
+    // unrolled so that the loads of several tiles are in flight together; the
+    // additions stay in tile order
+#pragma unroll 8
     for (int64_t tile = 0; tile < ws.ntiles; ++tile) {
       sb += ws.partB[(b * ws.ntiles + tile) * LN + r];
       sc += ws.partC[(b * ws.ntiles + tile) * LN + r];
@@ -620,6 +623,7 @@ __global__ void __launch_bounds__(256) bwd_reduce_tok_kernel(BwdArgs a, BwdWs ws
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
     const int64_t b = i / a.L, r = i % a.L;
     float sd = 0.0f;
+#pragma unroll 8
     for (int64_t tile = 0; tile < ws.ntiles; ++tile) sd += ws.partTok[(b * ws.ntiles + tile) * a.L + r];
     store_io((IO *)a.ddelta, i, sd);
   }
@@ -697,11 +701,13 @@ __global__ void __launch_bounds__(256) bwd_reduce_params_kernel(BwdArgs a, BwdWs
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < DN) {
     float s = 0.0f;
+#pragma unroll 8
     for (int64_t r = 0; r < R; ++r) s += ws.partA[r * DN + i];
     a.dA[i] = s;
   }
   if (i < a.D) {
     float sd = 0.0f, sb = 0.0f;
+#pragma unroll 8
     for (int64_t r = 0; r < R; ++r) {
       sd += ws.partD[r * a.D + i];
       sb += ws.partBias[r * a.D + i];

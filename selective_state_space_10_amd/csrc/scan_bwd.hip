@@ -678,20 +678,42 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(BwdArgs a, BwdWs ws) {
 }
 
 // Convolution taps and bias: sum of the per-block partials in a fixed order.
-__global__ void __launch_bounds__(256) conv_reduce_kernel(BwdArgs a, BwdWs ws) {
+// Taps and bias of the convolution: sums of the per-(row, block) partials.
+// A workgroup covers 64 channels; its 16 waves take every 16th partial row
+// each (in increasing order), and the 16 group sums are then added in group
+// order, so the result does not depend on timing.
+constexpr int kConvRedGroups = 16;
+__global__ void __launch_bounds__(64 * kConvRedGroups) conv_reduce_kernel(BwdArgs a, BwdWs ws) {
   constexpr int W = kMaxConv;
-  const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (d >= a.D) return;
-  const int K = a.conv_k;
+  constexpr int NG = kConvRedGroups;
+  static_assert(W == 4, "a partial row's taps are one float4");
+  __shared__ float S[NG][W + 1][64];
+  const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int64_t d = (int64_t)blockIdx.x * 64 + c;
+  const bool dv = d < a.D;
+  const int64_t dc = dv ? d : a.D - 1;
   const int64_t R = a.B * ws.nrb;
   float sw[W] = {0.f, 0.f, 0.f, 0.f}, sb = 0.0f;
-  for (int64_t r = 0; r < R; ++r) {
-#pragma unroll
-    for (int k = 0; k < W; ++k) sw[k] += ws.cwp[(r * a.D + d) * W + k];
-    sb += ws.cbp[r * a.D + d];
+#pragma unroll 4
+  for (int64_t r = q; r < R; r += NG) {
+    const float4 w4 = *(const float4 *)&ws.cwp[(r * a.D + dc) * W];
+    sw[0] += w4.x, sw[1] += w4.y, sw[2] += w4.z, sw[3] += w4.w;
+    sb += ws.cbp[r * a.D + dc];
   }
-  for (int k = 0; k < K; ++k) a.dconv_w[d * K + k] = sw[k + W - K];
-  if (a.dconv_b) a.dconv_b[d] = sb;
+#pragma unroll
+  for (int k = 0; k < W; ++k) S[q][k][c] = sw[k];
+  S[q][W][c] = sb;
+  __syncthreads();
+  if (q != 0 || !dv) return;
+  float tw[W] = {0.f, 0.f, 0.f, 0.f}, tb = 0.0f;
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int k = 0; k < W; ++k) tw[k] += S[g][k][c];
+    tb += S[g][W][c];
+  }
+  const int K = a.conv_k;
+  for (int k = 0; k < K; ++k) a.dconv_w[d * K + k] = tw[k + W - K];
+  if (a.dconv_b) a.dconv_b[d] = tb;
 }
 
 // dA, dD, d bias: sum of the partials over batch rows and segments.
@@ -747,7 +769,8 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
     const unsigned dt = (unsigned)((a.D + 255) / 256);
     hipLaunchKernelGGL((conv_bwd_kernel<IO>), dim3(dt, (unsigned)a.B, (unsigned)ws.nrb), dim3(256), 0, s, a, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(conv_reduce_kernel, dim3(dt), dim3(256), 0, s, a, ws);
+    hipLaunchKernelGGL(conv_reduce_kernel, dim3((unsigned)((a.D + 63) / 64)), dim3(64 * kConvRedGroups), 0, s, a,
+                       ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.flags & kFlagDeltaPerToken) {

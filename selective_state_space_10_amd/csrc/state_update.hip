@@ -23,14 +23,13 @@ constexpr int kDecodeSPL = 8;
 // ZOH: exact zero-order-hold input term expm1(dt A)/A * B * u (reading
 // guide, "Yöntem", discretisation of B) instead of dt * B * u.
 template <typename IO, int N, bool ZOH>
-__global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a, int64_t b0) {
+__global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   constexpr int SPL = N < kDecodeSPL ? N : kDecodeSPL;  // states per lane
   constexpr int LPC = N / SPL;                          // lanes per channel
   constexpr int NV = SPL >= 4 ? SPL / 4 : 0;            // 16-byte pieces per lane
   // grid: x covers the channels of one batch row (LPC lanes each), y the rows
-  // from b0 on
   const int gid = blockIdx.x * 256 + threadIdx.x;
-  const int64_t b = b0 + blockIdx.y;
+  const int64_t b = blockIdx.y;
   const int64_t dd = gid / LPC;
   const int g = gid % LPC;
   const bool valid = dd < a.D;
@@ -92,17 +91,12 @@ template <typename IO, int N>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
   constexpr int LPC = N < kDecodeSPL ? 1 : N / kDecodeSPL;
   const int64_t threads = a.D * LPC;  // per batch row
-  constexpr int64_t kRows = 65535;    // batch rows per launch (grid y)
-  for (int64_t b0 = 0; b0 < a.B; b0 += kRows) {
-    const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)(a.B - b0 < kRows ? a.B - b0 : kRows));
-    if (a.flags & kFlagZoh)
-      hipLaunchKernelGGL((decode_kernel<IO, N, true>), grid, dim3(256), 0, s, a, b0);
-    else
-      hipLaunchKernelGGL((decode_kernel<IO, N, false>), grid, dim3(256), 0, s, a, b0);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)a.B);
+  if (a.flags & kFlagZoh)
+    hipLaunchKernelGGL((decode_kernel<IO, N, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<IO, N, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 template <typename IO>

@@ -55,6 +55,14 @@ def test_small_channel_counts_and_short_rows(ssm, B, L, D, N, dtype):
     _check_bwd(ssm, p, TOL[dtype], seed=B)
 
 
+def test_more_batch_rows_than_one_grid_row_range(ssm):
+    """65537 batch rows (more than a 16-bit grid index): forward and backward
+    cover every row."""
+    p = _problem(65537, 3, 8, 4, torch.bfloat16, seed=65, h0=True)
+    _check_fwd(ssm, p, TOL[torch.bfloat16])
+    _check_bwd(ssm, p, TOL[torch.bfloat16], seed=65)
+
+
 @pytest.mark.parametrize("opts", [dict(), dict(zoh=True), dict(reverse=True, tok=True)],
                          ids=["plain", "zoh", "reverse-per-token"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])

@@ -272,8 +272,7 @@ def test_decode_no_optionals(ssm):
 
 @pytest.mark.parametrize("N", [4, 16])
 def test_decode_more_rows_than_one_grid(ssm, N):
-    """More batch rows than one launch's grid holds (65535): the rows past it
-    go to further launches with a row offset."""
+    """65537 batch rows (more than a 16-bit grid index): every row is updated."""
     d = decode_inputs(65537, 8, N, 2, torch.bfloat16, seed=33)
     _decode_check(ssm, d, 2, TOL[torch.bfloat16])
 

@@ -320,6 +320,28 @@ def bench_decode(args, zoh=False):
                                            "unit": "GB/s", "kernel_ms": ms_one}}}
 
 
+def _alu_floor_bwd(Bsz, L, D, N, ms_launch):
+    """The backward's vector-ALU floor: per state update 14 FP32 operations and
+    one exp2 (recompute: dt*A', dt*u*B, the state FMA; adjoint: e*C + lambda and
+    the decay product; C*h for dz; the dB and dC contributions and their adds in
+    the sums over channels; lambda*B for du; lambda*h_prev, its A-weighted sum for
+    ddelta and its dt-weighted sum for dA); per (b,t,d), shared by the N states,
+    24 FP32 operations and 6 transcendentals (softplus and its derivative
+    sigma(s), sigma(z) for the gate and its derivative, the input gradients
+    du, ddelta, dz, and the dD and dbias sums).  A sequence split's first pass
+    is extra work the floor does not count."""
+    upd, td = Bsz * L * D * N, Bsz * L * D
+    floor_s = (upd * (14 / VALU_OPS_PER_S + 1 / TRANS_OPS_PER_S)
+               + td * (24 / VALU_OPS_PER_S + 6 / TRANS_OPS_PER_S))
+    achieved = upd / (ms_launch * 1e-3) / 1e9
+    peak = upd / floor_s / 1e9
+    return {"kind": "vector-ALU floor of the backward (14 FP32 ops + 1 exp2 per state update, "
+                    "24 FP32 ops + 6 transcendentals per (b,t,d)) at the published fp32 vector rate, "
+                    "transcendentals at a quarter of it",
+            "achieved": achieved, "peak": peak, "unit": "Gupdates/s", "frac": achieved / peak,
+            "floor_ms": floor_s * 1e3}
+
+
 def bench_bwd(args, idx, name, conv=0):
     """Backward of workload ``idx`` (one forward with chunk states runs first,
     outside the timed steps); ``conv``: with the fused convolution of that width."""
@@ -366,7 +388,8 @@ def bench_bwd(args, idx, name, conv=0):
                                             "prewarm_steps": _time_launches.prewarm_steps},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                         "algorithmic_bytes": nbytes, "kernel_ms": ms_launch}}
+                         "algorithmic_bytes": nbytes, "kernel_ms": ms_launch,
+                         **({} if conv else {"alu": _alu_floor_bwd(Bsz, L, D, N, ms_launch)})}}
 
 
 def main():

@@ -35,7 +35,7 @@
  *     bf16 outputs are rounded to nearest even.
  *   - Every pointer must be 16-byte aligned (ssm_state_update relaxes this,
  *     see there); dim must be a multiple of 8;
- *     dstate must be 1, 2, 4, 8 or 16; batch, seqlen, dim >= 1.
+ *     dstate must be 1, 2, 4, 8 or 16; batch, seqlen, dim >= 1; batch <= 2^31 - 1.
  *   - The caller owns all memory.  The library never allocates, frees or
  *     synchronises device memory; it enqueues kernels on hip_stream (a
  *     hipStream_t; NULL = the default stream) and returns at once.
@@ -62,7 +62,7 @@ typedef enum ssm_status {
   SSM_OK = 0,
   SSM_ERR_NULL_ARG = 1,    /* a required pointer is NULL, or an optional pair is inconsistent */
   SSM_ERR_BAD_SHAPE = 2,   /* a size is < 1 (or would overflow 64-bit offsets) */
-  SSM_ERR_UNSUPPORTED = 3, /* dstate not in {1,2,4,8,16}, dim % 8 != 0, unknown io_dtype */
+  SSM_ERR_UNSUPPORTED = 3, /* dstate not in {1,2,4,8,16}, dim % 8 != 0, batch >= 2^31, unknown io_dtype */
   SSM_ERR_ALIGNMENT = 4,   /* a pointer is not 16-byte aligned */
   SSM_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns */
   SSM_ERR_HIP = 6          /* the HIP runtime reported an error while enqueuing */

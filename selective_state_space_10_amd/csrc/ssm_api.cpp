@@ -41,6 +41,8 @@ int check_sizes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int 
   int64_t bl, bld, bln;
   if (!mul_ok(batch, seqlen, &bl) || !mul_ok(bl, dim, &bld) || !mul_ok(bl, dstate, &bln))
     return fail(SSM_ERR_BAD_SHAPE, "sizes overflow 64-bit element offsets");
+  if (batch > 0x7fffffff)  // batch rows are a grid dimension of every launch
+    return fail(SSM_ERR_UNSUPPORTED, "batch=%lld exceeds 2^31-1", (long long)batch);
   if (!valid_dstate(dstate))
     return fail(SSM_ERR_UNSUPPORTED, "dstate=%lld not in {1,2,4,8,16}", (long long)dstate);
   if (dim % 8 != 0) return fail(SSM_ERR_UNSUPPORTED, "dim=%lld is not a multiple of 8", (long long)dim);

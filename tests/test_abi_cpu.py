@@ -97,6 +97,7 @@ def _fwd(lib, B=1, L=16, D=8, N=4, io=0, **kw):
     (dict(B=0), BAD_SHAPE), (dict(L=0), BAD_SHAPE), (dict(D=0), BAD_SHAPE), (dict(N=0), BAD_SHAPE),
     (dict(L=-3), BAD_SHAPE), (dict(B=1 << 40, L=1 << 40), BAD_SHAPE),
     (dict(N=3), UNSUPPORTED), (dict(N=32), UNSUPPORTED), (dict(D=12), UNSUPPORTED),
+    (dict(B=1 << 31), UNSUPPORTED),
     (dict(io=2), UNSUPPORTED)])
 def test_fwd_rejects_bad_sizes(lib, sizes, status):
     assert _fwd(lib, **sizes) == status

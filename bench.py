@@ -43,6 +43,11 @@ WORKLOAD_NAMES = ["mamba-370m-layer-fwd", "mamba-2.8b-layer-fwd", "decode-state-
                   "mamba-370m-layer-bidirectional", "decode-state-update-zoh",
                   "mamba-370m-layer-fwd-conv4", "mamba-370m-layer-bwd-conv4"]
 METRIC = "selective-scan fwd tokens·channels/s and HBM GB/s (% of peak), Mamba-370m shape"
+# The only throughput figure the source pages give for the method is relative and
+# names no hardware, precision or workload: context beside the kernel's rate, not
+# a number it can be compared with (reading guide of arXiv 2312.00752, "Sonuçlar").
+PAGES_CLAIM = {"claim": "inference throughput up to 5x that of Transformers of similar size",
+               "hardware": None, "workload": None, "comparable": False}
 UNIT = "tokens*channels/s"
 
 
@@ -258,6 +263,8 @@ def bench_fwd(args, idx, name, zoh=False, per_token=False, bidirectional=False, 
         pc = workload_inputs(idx, device="cuda", seed=idx)
         pc = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in pc.items()}
         line["cpu_baseline"] = _cpu_baseline_fwd(pc)
+    if name == "mamba-370m-layer-fwd":
+        line["context"] = PAGES_CLAIM
     return line
 
 

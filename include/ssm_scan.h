@@ -223,7 +223,8 @@ int64_t ssm_scan_bwd_conv_workspace_bytes(int64_t batch, int64_t seqlen, int64_t
                                           int64_t dstate, int io_dtype);
 
 /*
- * Backward of ssm_scan_fwd_conv.  u is recomputed from x.  Outputs as for
+ * Backward of ssm_scan_fwd_conv.  u is recomputed from x (the convolution's
+ * pre-activation is written to the workspace first).  Outputs as for
  * ssm_scan_bwd_ex with du replaced by dx (B,L,D) io_dtype, plus dconv_w (D,K)
  * fp32 and dconv_b (D) fp32 (required iff conv_b != NULL), all overwritten:
  *   g = dLoss/du * silu'(pre),  dx[b,t,d] = sum_k conv_w[d,k] g[b, t+(K-1)-k, d],

@@ -64,6 +64,7 @@ struct BwdWs {
   float *lamloc, *carry;    // (B, nseg, D, N): sequence split only
   float *dsum;              // (B, nseg, D)
   float *gconv;             // (B, L, D): gradient at the convolution's pre-activation
+  float *cpre;              // (B, L, D): the convolution's pre-activation, for the recompute of u
   float *cwp, *cbp;         // (B, nrb, D, kMaxConv) and (B, nrb, D): conv tap and bias partials
   int64_t ntiles, nseg, seg_len, nrb;
 };
@@ -118,10 +119,11 @@ BwdWs carve_ws(void *base, int64_t B, int64_t L, int64_t D, int64_t N, int64_t *
   }
   if (conv) {
     w.gconv = take(B * L * D * 4);
+    w.cpre = take(B * L * D * 4);
     w.cwp = take(B * w.nrb * D * kMaxConv * 4);
     w.cbp = take(B * w.nrb * D * 4);
   } else {
-    w.gconv = w.cwp = w.cbp = nullptr;
+    w.gconv = w.cpre = w.cwp = w.cbp = nullptr;
   }
   if (total) *total = off;
   return w;
@@ -133,7 +135,8 @@ BwdWs carve_ws(void *base, int64_t B, int64_t L, int64_t D, int64_t N, int64_t *
 // blockIdx.z + 1 is the segment.
 // ZOH: the exact zero-order-hold input term coef = expm1(dt A)/A, whose
 // derivatives are d coef/d dt = exp(dt A) and d coef/d A = dt^2 psi(dt A).
-// CONV: u is recomputed as silu(conv(x)) from the causal convolution's input,
+// CONV: u is recomputed as silu(pre) from the convolution's pre-activation
+// (written by conv_pre_kernel before this kernel),
 // and the gradient is written at the convolution's pre-activation (the
 // convolution's own backward runs afterwards).
 // Reverse direction and one step size per token are runtime flags; steps are
@@ -184,9 +187,6 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
   const bool rev = (a.flags & kFlagReverse) != 0;
   const bool tok = (a.flags & kFlagDeltaPerToken) != 0;
   auto mrow = [&](int64_t t) { return rev ? L - 1 - t : t; };  // memory row of scan step t
-  constexpr int XK = CONV ? kMaxConv : 1;
-  const int ck = CONV ? a.conv_k : 0;
-  const IO *__restrict__ xin = (const IO *)a.x;
 
   __shared__ __attribute__((aligned(16))) float2 P[T][CPW];  // (dt, dt*u), or (dt, u) with ZOH
   __shared__ __attribute__((aligned(16))) float SGC[CONV ? T : 1][CPW];  // silu' at the conv output
@@ -216,22 +216,6 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
     const float4 v = *(const float4 *)(a.bias + dgc);
     bias4[0] = v.x, bias4[1] = v.y, bias4[2] = v.z, bias4[3] = v.w;
   }
-  // convolution taps (zero past the width) and bias per channel, in LDS: read in
-  // the prologue only, so they hold no registers through the recurrence
-  __shared__ __attribute__((aligned(16))) float CWB[CONV ? CPW : 1][kMaxConv + 1];
-  if (CONV) {
-    for (int i = tid; i < CPW * (kMaxConv + 1); i += NT) {
-      const int c = i / (kMaxConv + 1), kk = i % (kMaxConv + 1);
-      const int64_t dd = d0 + c < D ? d0 + c : D - 1;
-      float v = 0.0f;
-      if (kk < ck)
-        v = a.conv_w[dd * ck + kk];
-      else if (kk == kMaxConv && a.conv_b)
-        v = a.conv_b[dd];
-      CWB[c][kk] = v;
-    }
-    __syncthreads();
-  }
 
   // --- sweep ownership: channel d0 + lane, slot s holds state w*NPL + (s ^ par)
   const int64_t d = d0 + lane;
@@ -259,7 +243,7 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
   float dD_acc = 0.0f, dbias_acc = 0.0f, dsum = 0.0f;
 
   raw_t r_dl[IPT], r_u[IPT], r_z[IPT], r_dy[IPT];
-  raw_t r_x[IPT][XK];
+  float4 r_p[CONV ? IPT : 1];  // with CONV: the convolution's pre-activation
   float r_b[BPT], r_c[BPT], r_h[NPL];
 
   auto load_chunk = [&](int64_t kc) {
@@ -271,13 +255,8 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
       const int64_t idx = r * D + dgc;
       r_dl[j] = tok ? V::splat(dl, r) : V::load(dl, idx);
       r_dy[j] = V::load(dyp, idx);
-      if (MODE == 0 && CONV) {  // the rows the causal convolution reads (forward direction only)
-        const int64_t tm = t < te ? t : te - 1;
-#pragma unroll
-        for (int kk = 0; kk < XK; ++kk) {
-          const int64_t ts = tm - (ck - 1) + kk;
-          r_x[j][kk] = (kk < ck && ts >= 0) ? V::load(xin, (row0 + ts) * D + dgc) : raw_t{};
-        }
+      if (MODE == 0 && CONV) {
+        r_p[CONV ? j : 0] = *(const float4 *)(ws.cpre + idx);
       } else if (MODE == 0) {
         r_u[j] = V::load(u, idx);
       }
@@ -308,17 +287,9 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
       const bool ok = gv && t0 + tl < te;  // padding steps and channels: dt = 0, e = 0
       const float4 r4 = V::cvt(r_dl[j]), g4 = V::cvt(r_dy[j]);
       float4 x4 = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (MODE == 0 && CONV) {  // u = silu(pre), pre = bias + sum_k w_k x[t - (K-1) + k]; keep silu'(pre)
-        const int cg = 4 * g;
-        float pre[4] = {CWB[cg][kMaxConv], CWB[cg + 1][kMaxConv], CWB[cg + 2][kMaxConv], CWB[cg + 3][kMaxConv]};
-#pragma unroll
-        for (int kk = 0; kk < XK; ++kk) {
-          const float4 xv = V::cvt(r_x[j][kk]);
-          pre[0] = fmaf(CWB[cg][kk], xv.x, pre[0]);
-          pre[1] = fmaf(CWB[cg + 1][kk], xv.y, pre[1]);
-          pre[2] = fmaf(CWB[cg + 2][kk], xv.z, pre[2]);
-          pre[3] = fmaf(CWB[cg + 3][kk], xv.w, pre[3]);
-        }
+      if (MODE == 0 && CONV) {  // u = silu(pre); keep silu'(pre)
+        const float4 p4 = r_p[CONV ? j : 0];
+        const float pre[4] = {p4.x, p4.y, p4.z, p4.w};
         float uv[4], sd[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -635,6 +606,42 @@ __global__ void __launch_bounds__(256) bwd_reduce_tok_kernel(BwdArgs a, BwdWs ws
 // Taps are padded at the front to width kMaxConv (zero taps), so the windows
 // are static.  One thread per (channel, batch row, block of kConvRows rows);
 // tap and bias sums are per-block partials.
+// The convolution's pre-activation for the backward's recompute of u:
+// pre[b,t,d] = bias_d + sum_k w[d,k] x[b, t-(K-1)+k, d] (rows before the first
+// are zero), one thread per channel and 64-row block, x read once through a
+// sliding window.
+template <typename IO>
+__global__ void __launch_bounds__(256) conv_pre_kernel(BwdArgs a, BwdWs ws) {
+  constexpr int W = kMaxConv;
+  const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t b = blockIdx.y, rb = blockIdx.z;
+  const int64_t L = a.L, D = a.D;
+  if (d >= D) return;  // no barrier in this kernel
+  const int K = a.conv_k;
+  float wp[W];  // padded taps: wp[k'] = w[k' - (W - K)] for k' >= W - K
+#pragma unroll
+  for (int k = 0; k < W; ++k) wp[k] = k >= W - K ? a.conv_w[d * K + k - (W - K)] : 0.0f;
+  const float cb = a.conv_b ? a.conv_b[d] : 0.0f;
+  const IO *xin = (const IO *)a.x;
+  const int64_t t0 = rb * kConvRows, t1 = t0 + kConvRows < L ? t0 + kConvRows : L;
+  const int64_t base = b * L;
+  float xw[W];  // xw[k'] = x[t - (W-1) + k']
+#pragma unroll
+  for (int j = 0; j < W - 1; ++j) {
+    const int64_t ts = t0 - (W - 1) + j;
+    xw[j] = ts >= 0 ? load_io(xin, (base + ts) * D + d) : 0.0f;
+  }
+  for (int64_t t = t0; t < t1; ++t) {
+    xw[W - 1] = load_io(xin, (base + t) * D + d);
+    float pre = cb;
+#pragma unroll
+    for (int k = 0; k < W; ++k) pre = fmaf(wp[k], xw[k], pre);
+    ws.cpre[(base + t) * D + d] = pre;
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) xw[j] = xw[j + 1];
+  }
+}
+
 template <typename IO>
 __global__ void __launch_bounds__(256) conv_bwd_kernel(BwdArgs a, BwdWs ws) {
   constexpr int W = kMaxConv;
@@ -752,6 +759,11 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nst = a.B * a.D * a.N;
     hipLaunchKernelGGL(bwd_seg_combine_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, a, ws);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (conv) {
+    hipLaunchKernelGGL((conv_pre_kernel<IO>), dim3((unsigned)((a.D + 255) / 256), (unsigned)a.B, (unsigned)ws.nrb),
+                       dim3(256), 0, s, a, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const dim3 grid(tiles, (unsigned)a.B, (unsigned)ws.nseg);

@@ -14,9 +14,10 @@ line (rank 0).
 ``--workload`` also accepts the other shapes and options (mamba-2.8b-layer-fwd,
 decode-state-update, million-length-fwd, million-length-bwd,
 mamba-370m-layer-bwd, the 370m forward with the exact zero-order hold, with one
-step size per token, or bidirectional, and the decode step with the exact
-hold); their lines use the same keys and are for reference, the default
-workload is the headline.
+step size per token, bidirectional or with the fused convolution, the 370m
+backward with the exact hold or the fused convolution, and the decode step with
+the exact hold); their lines use the same keys and are for reference, the
+default workload is the headline.
 """
 from __future__ import annotations
 
@@ -41,7 +42,7 @@ WORKLOAD_NAMES = ["mamba-370m-layer-fwd", "mamba-2.8b-layer-fwd", "decode-state-
                   "million-length-fwd", "million-length-bwd", "mamba-370m-layer-bwd",
                   "mamba-370m-layer-fwd-zoh", "mamba-370m-layer-fwd-token-delta",
                   "mamba-370m-layer-bidirectional", "decode-state-update-zoh",
-                  "mamba-370m-layer-fwd-conv4", "mamba-370m-layer-bwd-conv4"]
+                  "mamba-370m-layer-fwd-conv4", "mamba-370m-layer-bwd-conv4", "mamba-370m-layer-bwd-zoh"]
 METRIC = "selective-scan fwd tokens·channels/s and HBM GB/s (% of peak), Mamba-370m shape"
 # The only throughput figure the source pages give for the method is relative and
 # names no hardware, precision or workload: context beside the kernel's rate, not
@@ -349,9 +350,10 @@ def _alu_floor_bwd(Bsz, L, D, N, ms_launch):
             "floor_ms": floor_s * 1e3}
 
 
-def bench_bwd(args, idx, name, conv=0):
+def bench_bwd(args, idx, name, conv=0, zoh=False):
     """Backward of workload ``idx`` (one forward with chunk states runs first,
-    outside the timed steps); ``conv``: with the fused convolution of that width."""
+    outside the timed steps); ``conv``: with the fused convolution of that width;
+    ``zoh``: with the exact zero-order hold."""
     import torch
 
     import selective_state_space_10_amd as m
@@ -365,7 +367,7 @@ def bench_bwd(args, idx, name, conv=0):
                                    p["z"], p["delta_bias"], True, None, save_chunk_states=True)
     else:
         y, _, cs = m.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
-                              p["delta_bias"], True, None, save_chunk_states=True)
+                              p["delta_bias"], True, None, save_chunk_states=True, zoh=zoh)
     dy = cotangent(y, idx)
     del y
 
@@ -375,7 +377,7 @@ def bench_bwd(args, idx, name, conv=0):
                             p["delta_bias"], True, None, cs, dy)
         else:
             m.scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
-                       p["delta_bias"], True, None, cs, dy)
+                       p["delta_bias"], True, None, cs, dy, zoh=zoh)
 
     ms_step, ms_launch, wall = _time_launches(step, args.steps, args.warmup, [0])
     Bsz, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
@@ -396,7 +398,7 @@ def bench_bwd(args, idx, name, conv=0):
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                          "algorithmic_bytes": nbytes, "kernel_ms": ms_launch,
-                         **({} if conv else {"alu": _alu_floor_bwd(Bsz, L, D, N, ms_launch)})}}
+                         **({} if conv or zoh else {"alu": _alu_floor_bwd(Bsz, L, D, N, ms_launch)})}}
 
 
 def main():
@@ -438,6 +440,8 @@ def main():
         line = bench_fwd(args, 1, wl, conv=4)
     elif wl == "mamba-370m-layer-bwd-conv4":
         line = bench_bwd(args, 1, wl, conv=4)
+    elif wl == "mamba-370m-layer-bwd-zoh":
+        line = bench_bwd(args, 1, wl, zoh=True)
     else:
         line = bench_bwd(args, 4, wl)
     print(json.dumps(line), flush=True)

@@ -448,8 +448,10 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
     if (kc > 0) load_chunk(kc - 1);
     __syncthreads();
 
-    // Recompute the chunk's states and decay factors.
-    float Hh[T][NPL], Ha[T][NPL];
+    // Recompute the chunk's states and decay factors.  With ZOH the decay
+    // factors are formed again in the sweep instead: the exact hold's extra
+    // terms leave no room for both in registers (they would be spilled).
+    float Hh[T][NPL], Ha[ZOH ? 1 : T][NPL];
     {
       float h[NPL];
 #pragma unroll
@@ -465,7 +467,7 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
           const float cf = ZOH ? zoh_coef(p.x, p.x * An[s], da, Ainv[s]) : 1.0f;
           h[s] = fmaf(da, h[s], ZOH ? cf * p.y * bv[s] : p.y * bv[s]);
           Hh[tl][s] = h[s];
-          Ha[tl][s] = da;
+          if (!ZOH) Ha[ZOH ? 0 : tl][s] = da;
         }
       }
     }
@@ -486,7 +488,7 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
           const float ht = Hh[tl][s];
           const float hp = tl > 0 ? Hh[tl > 0 ? tl - 1 : 0][s] : hs[s];
           const float lt = fmaf(e, cv[s], lam[s]);
-          const float da = Ha[tl][s];
+          const float da = ZOH ? fast_exp2(p.x * Ap[s]) : Ha[ZOH ? 0 : tl][s];
           pre = fmaf(cv[s], ht, pre);
           cC[s] = e * ht;
           lam[s] = da * lt;

@@ -35,7 +35,8 @@
  *     bf16 outputs are rounded to nearest even.
  *   - Every pointer must be 16-byte aligned (ssm_state_update relaxes this,
  *     see there); dim must be a multiple of 8;
- *     dstate must be 1, 2, 4, 8 or 16; batch, seqlen, dim >= 1; batch <= 2^31 - 1.
+ *     dstate must be 1, 2, 4, 8 or 16; batch, seqlen, dim >= 1; batch <= 2^31 - 1;
+ *     dim <= 2^36 (the channel tiles of a batch row are a grid dimension).
  *   - The caller owns all memory.  The library never allocates, frees or
  *     synchronises device memory; it enqueues kernels on hip_stream (a
  *     hipStream_t; NULL = the default stream) and returns at once.
@@ -62,7 +63,8 @@ typedef enum ssm_status {
   SSM_OK = 0,
   SSM_ERR_NULL_ARG = 1,    /* a required pointer is NULL, or an optional pair is inconsistent */
   SSM_ERR_BAD_SHAPE = 2,   /* a size is < 1 (or would overflow 64-bit offsets) */
-  SSM_ERR_UNSUPPORTED = 3, /* dstate not in {1,2,4,8,16}, dim % 8 != 0, batch >= 2^31, unknown io_dtype */
+  SSM_ERR_UNSUPPORTED = 3, /* dstate not in {1,2,4,8,16}, dim % 8 != 0, batch >= 2^31, dim > 2^36,
+                              unknown io_dtype */
   SSM_ERR_ALIGNMENT = 4,   /* a pointer is not 16-byte aligned */
   SSM_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns */
   SSM_ERR_HIP = 6          /* the HIP runtime reported an error while enqueuing */
@@ -120,6 +122,28 @@ int64_t ssm_scan_chunk_states_bytes(int64_t batch, int64_t seqlen, int64_t dim, 
  * workspace may be NULL).  Returns -1 on invalid sizes. */
 int64_t ssm_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                                      int io_dtype);
+
+/*
+ * How ssm_scan_fwd (and its _ex and _conv forms) would run these sizes on the
+ * current device: the kernel, the channels each workgroup owns, and the
+ * sequence split.  A host-side query: it launches nothing and touches no
+ * device memory (it reads the device's compute-unit count once per process;
+ * without a device it assumes 256).  Tests use it to show which kernel
+ * variant a shape reaches.  conv_width is 0 for the plain scan, else the
+ * width of the fused convolution.  Returns SSM_OK and fills *plan, or an
+ * error status as for the forward itself (nothing written on error).
+ */
+typedef struct ssm_fwd_plan {
+  int32_t kernel;        /* 0: all-purpose kernel (every phase on every wave);
+                            1: wave-specialised kernel (16 states: recurrence
+                               waves and service waves) */
+  int32_t tile_channels; /* channels per workgroup: 16, 32, 64 or 80 */
+  int64_t segments;      /* sequence segments (1 = no split) */
+  int64_t segment_len;   /* steps per segment (0 = no split) */
+} ssm_fwd_plan;
+
+int ssm_scan_fwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                      int flags, int conv_width, ssm_fwd_plan *plan);
 
 /*
  * Forward selective scan (the recurrence above over all L steps).

@@ -6,9 +6,11 @@ shapes.  Softplus uses ``numpy.logaddexp(0, x)`` and the sigmoid uses
 ``scipy.special.expit``, so neither shares a formula with the C version.
 
 Same definition as ``ssm_oracle.c``: Mamba (Gu & Dao) per the reading guide's
-"Yöntem" discretisation equations and "Seçim Mekanizması (S6)" delta equation,
-the input term delta*B*u of the sequential loop quoted on the mamba-minimal
-news page, the D*u skip and SiLU gate of the Mamba block.
+"Yöntem" equations (zero-order hold of A, the linear recurrence of the state,
+the output as the state contracted with C) and its "Seçim Mekanizması (S6)"
+step-size equation, with the first-order input term delta*B*u (the reading
+taken for the discretisation of B), the D*u skip and the SiLU gate of the
+Mamba block.
 """
 from __future__ import annotations
 
@@ -73,12 +75,15 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
     for k, t in enumerate(order):
         if chunk_len and k % chunk_len == 0:
             chunks.append(h.copy())
-        decay = np.exp(dt[:, t, :, None] * A[None, :, :])
-        inject = _coef(dt[:, t], A, zoh) * u[:, t, :, None] * B[:, t, None, :]
-        h = decay * h + inject
+        # one step of the discrete recurrence ("Yöntem"): the state decays by
+        # exp(dt A) per (b, d, n) and takes in the input term coef * B_t * u_t
+        Abar = np.exp(dt[:, t, :, None] * A[None, :, :])
+        Bbar_u = (_coef(dt[:, t], A, zoh) * B[:, t, None, :]) * u[:, t, :, None]
+        h = Abar * h + Bbar_u
         if return_states:
             states[:, k] = h
-        y[:, t, :] = np.einsum("bdn,bn->bd", h, C[:, t, :])
+        # output: the state contracted with C_t over the state index
+        y[:, t, :] = (h * C[:, t][:, None, :]).sum(axis=2)
     if D is not None:
         y = y + D[None, None, :] * u
     if z is not None:
@@ -155,7 +160,7 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delt
     dt = np.logaddexp(0.0, s) if delta_softplus else s
     new = (np.exp(dt[:, :, None] * A[None]) * state
            + _coef(dt, A, zoh) * u[:, :, None] * B[:, None, :])
-    y = np.einsum("bdn,bn->bd", new, C)
+    y = (new * C[:, None, :]).sum(axis=2)
     if D is not None:
         y = y + D * u
     if z is not None:

@@ -14,7 +14,14 @@ EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_error", "ssm_scan_c
            "ssm_scan_chunk_states_bytes", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd",
            "ssm_scan_fwd_ex", "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_ex",
            "ssm_state_update", "ssm_state_update_ex", "ssm_scan_fwd_conv",
-           "ssm_scan_bwd_conv_workspace_bytes", "ssm_scan_bwd_conv")
+           "ssm_scan_bwd_conv_workspace_bytes", "ssm_scan_bwd_conv", "ssm_scan_fwd_plan")
+
+
+class FwdPlan(ctypes.Structure):
+    """ssm_fwd_plan: kernel (0 all-purpose, 1 wave-specialised), channels per
+    workgroup, sequence segments and their length."""
+    _fields_ = [("kernel", ctypes.c_int32), ("tile_channels", ctypes.c_int32),
+                ("segments", ctypes.c_int64), ("segment_len", ctypes.c_int64)]
 
 # option bits of the *_ex entry points
 FLAG_ZOH = 1
@@ -75,6 +82,8 @@ def load() -> ctypes.CDLL:
     # ddelta_bias, dh0, workspace
     lib.ssm_scan_bwd_conv.argtypes = [I64] * 4 + [INT] + [P] * 3 + [INT] + [P] * 7 + [INT] \
         + [P] * 16 + [I64, P, INT]
+    lib.ssm_scan_fwd_plan.restype = INT
+    lib.ssm_scan_fwd_plan.argtypes = [I64] * 4 + [INT, INT, INT, ctypes.POINTER(FwdPlan)]
     _lib = lib
     return lib
 

@@ -72,6 +72,18 @@ struct DecodeArgs {
   void *y;
 };
 
+// Launch plan of a forward call (kernel kind, channels per workgroup,
+// sequence split), as the launcher follows it on the current device.
+constexpr int kPlanAllPurpose = 0;       // fwd_kernel: every phase on every wave
+constexpr int kPlanWaveSpecialised = 1;  // fwd_ws_kernel: recurrence and service waves
+struct FwdPlan {
+  int kernel;
+  int tile_channels;
+  int64_t segments;     // 1 = no sequence split
+  int64_t segment_len;  // steps per segment (0 = no split)
+};
+FwdPlan plan_fwd(const FwdArgs &a, int io_dtype);
+
 int64_t fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype);
 int64_t bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype);
 int64_t bwd_conv_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype);

@@ -867,41 +867,86 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename IO, int N>
-static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
+// The launch plan of a forward call: which kernel, how many channels per
+// workgroup, and the sequence split.  The launcher follows it and
+// ssm_scan_fwd_plan reports it, so the two cannot disagree.
+template <int N>
+static FwdPlan plan_fwd_t(const FwdArgs &a, int64_t io_bytes) {
   constexpr int NPL = N >= 2 ? 2 : 1;
   constexpr int mincpw = 64 * NPL / N > 16 ? 64 * NPL / N : 16;
   // options use one tile width (fewer instantiations); the plain scan picks its own
   constexpr int OCPW = mincpw > 32 ? 64 : 32;
+  FwdPlan pl{};
+  pl.segment_len = split_len(a.B, a.L, a.D, io_bytes);
+  pl.segments = pl.segment_len ? (a.L + pl.segment_len - 1) / pl.segment_len : 1;
+  if (N == 16 && pl.segment_len == 0 && a.L <= ws_max_rows(a.D, io_bytes)) {
+    // 16 states, no sequence split, and every row of a (B,L,D) array within
+    // 32-bit offsets: the wave-specialised kernel, also for the options
+    pl.kernel = kPlanWaveSpecialised;
+    int cpw = pick_cpw<N>(a);
+    if (cpw == 80 && a.conv_k) cpw = 32;  // the convolution variant needs more than 128 registers
+    if (cpw == 16) cpw = 32;              // (a tuning override; 32 is the narrowest tile here)
+    pl.tile_channels = cpw;
+    return pl;
+  }
+  int cpw;
+  if (a.flags || a.conv_k) {
+    cpw = OCPW;
+  } else {
+    const int c = pick_cpw<N>(a);
+    cpw = (mincpw <= 16 && c == 16) ? 16 : (mincpw <= 32 && c == 32) ? 32 : 64;
+  }
+  if (N == 16 && pl.segment_len) {  // both passes of a split: the wave-specialised kernel, 64-channel tiles
+    pl.kernel = kPlanWaveSpecialised;
+    pl.tile_channels = 64;
+  } else {
+    pl.kernel = kPlanAllPurpose;
+    pl.tile_channels = cpw;
+  }
+  return pl;
+}
+
+static FwdPlan plan_fwd_n(const FwdArgs &a, int64_t io_bytes) {
+  switch (a.N) {
+    case 1: return plan_fwd_t<1>(a, io_bytes);
+    case 2: return plan_fwd_t<2>(a, io_bytes);
+    case 4: return plan_fwd_t<4>(a, io_bytes);
+    case 8: return plan_fwd_t<8>(a, io_bytes);
+    default: return plan_fwd_t<16>(a, io_bytes);
+  }
+}
+
+FwdPlan plan_fwd(const FwdArgs &a, int io_dtype) { return plan_fwd_n(a, io_dtype == 0 ? 4 : 2); }
+
+template <typename IO, int N>
+static hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t s) {
+  const FwdPlan pl = plan_fwd_t<N>(a, sizeof(IO));
+  const bool zoh = (a.flags & kFlagZoh) != 0;
   if constexpr (N == 16) {
-    // 64-channel tiles in one round over the CUs and no sequence split: the
-    // wave-specialised kernel, also for the options it implements
-    // (unless a row of an array spans 2^31 bytes: then fwd_kernel, 64-bit offsets)
-    if (split_len(a.B, a.L, a.D, sizeof(IO)) == 0 && a.L <= ws_max_rows(a.D, sizeof(IO))) {
-      const bool zoh = (a.flags & kFlagZoh) != 0;
-      int cpw = pick_cpw<N>(a);
-      if (cpw == 80 && a.conv_k) cpw = 32;  // the convolution variant needs more than 128 registers
+    if (pl.kernel == kPlanWaveSpecialised && pl.segments == 1) {
+      const int cpw = pl.tile_channels;
+      const dim3 grid((unsigned)((a.D + cpw - 1) / cpw), (unsigned)a.B, 1);
       if (cpw == 64) {
-        const dim3 grid((unsigned)((a.D + 63) / 64), (unsigned)a.B, 1);
         zoh ? launch_ws<IO, 64, 0, true>(a, grid, s) : launch_ws<IO, 64, 0, false>(a, grid, s);
       } else if (cpw == 80) {
-        const dim3 grid((unsigned)((a.D + 79) / 80), (unsigned)a.B, 1);
         zoh ? launch_ws<IO, 80, 0, true>(a, grid, s) : launch_ws<IO, 80, 0, false>(a, grid, s);
       } else {  // 32-channel tiles: several workgroups per CU
-        const dim3 grid((unsigned)((a.D + 31) / 32), (unsigned)a.B, 1);
         zoh ? launch_ws<IO, 32, 0, true>(a, grid, s) : launch_ws<IO, 32, 0, false>(a, grid, s);
       }
       return hipGetLastError();
     }
   }
-  if (a.flags & kFlagZoh) return launch_fwd_cpw<IO, N, OCPW, true, true>(a, s);
+  // the all-purpose kernel, or a split sequence (launch_fwd_cpw runs both passes)
+  constexpr int NPL = N >= 2 ? 2 : 1;
+  constexpr int mincpw = 64 * NPL / N > 16 ? 64 * NPL / N : 16;
+  constexpr int OCPW = mincpw > 32 ? 64 : 32;
+  if (zoh) return launch_fwd_cpw<IO, N, OCPW, true, true>(a, s);
   if (a.flags || a.conv_k) return launch_fwd_cpw<IO, N, OCPW, false, true>(a, s);
-  const int cpw = pick_cpw<N>(a);
   if constexpr (mincpw <= 16) {
-    if (cpw == 16) return launch_fwd_cpw<IO, N, 16, false, false>(a, s);
+    if (pl.tile_channels == 16) return launch_fwd_cpw<IO, N, 16, false, false>(a, s);
   }
   if constexpr (mincpw <= 32) {
-    if (cpw == 32) return launch_fwd_cpw<IO, N, 32, false, false>(a, s);
+    if (pl.tile_channels == 32) return launch_fwd_cpw<IO, N, 32, false, false>(a, s);
   }
   return launch_fwd_cpw<IO, N, 64, false, false>(a, s);
 }

@@ -43,6 +43,8 @@ int check_sizes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int 
     return fail(SSM_ERR_BAD_SHAPE, "sizes overflow 64-bit element offsets");
   if (batch > 0x7fffffff)  // batch rows are a grid dimension of every launch
     return fail(SSM_ERR_UNSUPPORTED, "batch=%lld exceeds 2^31-1", (long long)batch);
+  if (dim > ((int64_t)1 << 36))  // channel tiles (and the decode's lanes) of a row are a grid dimension
+    return fail(SSM_ERR_UNSUPPORTED, "dim=%lld exceeds 2^36", (long long)dim);
   if (!valid_dstate(dstate))
     return fail(SSM_ERR_UNSUPPORTED, "dstate=%lld not in {1,2,4,8,16}", (long long)dstate);
   if (dim % 8 != 0) return fail(SSM_ERR_UNSUPPORTED, "dim=%lld is not a multiple of 8", (long long)dim);
@@ -109,6 +111,28 @@ int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim,
                                      int io_dtype) {
   if (check_sizes(batch, seqlen, dim, dstate, io_dtype) != SSM_OK) return -1;
   return ssm::bwd_workspace_bytes(batch, seqlen, dim, dstate, io_dtype);
+}
+
+int ssm_scan_fwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                      int flags, int conv_width, ssm_fwd_plan *plan) {
+  g_last_error[0] = 0;
+  int st = check_sizes(batch, seqlen, dim, dstate, io_dtype);
+  if (st != SSM_OK) return st;
+  if (plan == nullptr) return fail(SSM_ERR_NULL_ARG, "plan is NULL");
+  if (flags & ~(SSM_FLAG_ZOH | SSM_FLAG_REVERSE | SSM_FLAG_DELTA_PER_TOKEN | SSM_FLAG_ACCUMULATE))
+    return fail(SSM_ERR_UNSUPPORTED, "unknown flags 0x%x for the forward scan", flags);
+  if (conv_width < 0 || conv_width > ssm::kMaxConv)
+    return fail(SSM_ERR_UNSUPPORTED, "conv_width=%d not in 0..%d", conv_width, ssm::kMaxConv);
+  if (conv_width && (flags & SSM_FLAG_REVERSE))
+    return fail(SSM_ERR_UNSUPPORTED, "the fused convolution runs forward in time only");
+  ssm::FwdArgs a{};
+  a.B = batch, a.L = seqlen, a.D = dim, a.N = dstate, a.flags = flags, a.conv_k = conv_width;
+  const ssm::FwdPlan p = ssm::plan_fwd(a, io_dtype);
+  plan->kernel = p.kernel;
+  plan->tile_channels = p.tile_channels;
+  plan->segments = p.segments;
+  plan->segment_len = p.segment_len;
+  return SSM_OK;
 }
 
 int ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,

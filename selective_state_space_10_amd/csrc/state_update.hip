@@ -28,10 +28,11 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   constexpr int LPC = N / SPL;                          // lanes per channel
   constexpr int NV = SPL >= 4 ? SPL / 4 : 0;            // 16-byte pieces per lane
   // grid: x covers the channels of one batch row (LPC lanes each), y the rows
-  const int gid = blockIdx.x * 256 + threadIdx.x;
+  // 64-bit: dim * LPC may exceed 2^31 lanes per batch row
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t b = blockIdx.y;
-  const int64_t dd = gid / LPC;
-  const int g = gid % LPC;
+  const int64_t dd = gid / LPC;  // LPC is a power of two: shifts, not divisions
+  const int g = (int)(gid % LPC);
   const bool valid = dd < a.D;
   const int64_t d = valid ? dd : 0;
   const int64_t chc = b * a.D + d;  // b * D + d

@@ -48,6 +48,25 @@ def chunk_len() -> int:
     return int(_lib.load().ssm_scan_chunk_len())
 
 
+def scan_fwd_plan(batch, seqlen, dim, dstate, dtype=torch.float32, zoh=False, reverse=False,
+                  per_token=False, accumulate=False, conv_width=0) -> dict:
+    """How the forward would run these sizes on the current device (a host
+    query, nothing is launched): ``kernel`` ("all-purpose" or
+    "wave-specialised"), ``tile_channels``, ``segments`` and ``segment_len``."""
+    if dtype not in _IO:
+        raise TypeError(f"io dtype must be float32 or bfloat16, got {dtype}")
+    lib = _lib.load()
+    flags = ((_lib.FLAG_ZOH if zoh else 0) | (_lib.FLAG_REVERSE if reverse else 0)
+             | (_lib.FLAG_DELTA_PER_TOKEN if per_token else 0)
+             | (_lib.FLAG_ACCUMULATE if accumulate else 0))
+    plan = _lib.FwdPlan()
+    _lib.check(lib.ssm_scan_fwd_plan(batch, seqlen, dim, dstate, _IO[dtype], flags, conv_width,
+                                     plan))
+    return {"kernel": ("all-purpose", "wave-specialised")[plan.kernel],
+            "tile_channels": int(plan.tile_channels), "segments": int(plan.segments),
+            "segment_len": int(plan.segment_len)}
+
+
 def _flags(delta, u, zoh=False, reverse=False, accumulate=False):
     f = (_lib.FLAG_ZOH if zoh else 0) | (_lib.FLAG_REVERSE if reverse else 0)
     if accumulate:

@@ -97,7 +97,7 @@ def _fwd(lib, B=1, L=16, D=8, N=4, io=0, **kw):
     (dict(B=0), BAD_SHAPE), (dict(L=0), BAD_SHAPE), (dict(D=0), BAD_SHAPE), (dict(N=0), BAD_SHAPE),
     (dict(L=-3), BAD_SHAPE), (dict(B=1 << 40, L=1 << 40), BAD_SHAPE),
     (dict(N=3), UNSUPPORTED), (dict(N=32), UNSUPPORTED), (dict(D=12), UNSUPPORTED),
-    (dict(B=1 << 31), UNSUPPORTED),
+    (dict(B=1 << 31), UNSUPPORTED), (dict(D=(1 << 36) + 8), UNSUPPORTED),
     (dict(io=2), UNSUPPORTED)])
 def test_fwd_rejects_bad_sizes(lib, sizes, status):
     assert _fwd(lib, **sizes) == status
@@ -152,6 +152,59 @@ def test_decode_validation(lib):
     assert f(2, 8, 4, 0, FAKE + 2, *args[1:], 1, FAKE, None) == ALIGNMENT  # state
     assert f(2, 8, 4, 0, *args[:3], FAKE + 8, *args[4:], 1, FAKE, None) == ALIGNMENT  # A
     assert f(2, 8, 4, 1, *args[:4], FAKE + 1, *args[5:], 1, FAKE, None) == ALIGNMENT  # odd bf16
+
+
+def test_decode_rejects_dim_beyond_the_grid(lib):
+    """The decode kernel's lane index is 64-bit (more than 2^31 lanes per
+    batch row are addressed correctly); channel counts above 2^36, whose lanes
+    would not fit the grid, are rejected before any launch."""
+    f = lib.ssm_state_update
+    args = [FAKE] * 6 + [None, None, None]
+    assert f(1, (1 << 36) + 8, 16, 0, *args, 1, FAKE, None) == UNSUPPORTED
+    assert b"2^36" in lib.ssm_last_error()
+
+
+ZOH, REV, TOK, ACC = 1, 2, 4, 8
+
+
+@pytest.mark.parametrize("sizes,io,flags,conv,expect", [
+    ((8, 2048, 2048, 16), 0, 0, 0, (1, 64, 1)),        # Mamba-370m layer: 256 tiles of 64
+    ((8, 2048, 2048, 16), 0, ZOH, 4, (1, 64, 1)),
+    ((4, 4096, 5120, 16), 1, 0, 0, (1, 80, 1)),        # Mamba-2.8b layer: 256 tiles of 80
+    ((4, 4096, 5120, 16), 1, 0, 4, (1, 32, 1)),        # ... with the fused convolution
+    ((8, 40, 3336, 16), 0, 0, 0, (1, 32, 1)),          # 8 x 42 tiles of 80 > 256
+    ((8, 40, 3336, 16), 1, ZOH, 0, (1, 32, 1)),
+    ((8, 40, 3336, 16), 0, REV | TOK, 0, (1, 32, 1)),
+    ((1, 37, 20480, 16), 0, 0, 0, (1, 80, 1)),
+    ((1, 1 << 20, 1024, 16), 1, 0, 0, (1, 64, 16)),    # million-length: split into 16 segments
+    ((1, 65536, 8192, 16), 0, 0, 0, (0, 64, 1)),       # a row spans 2 GiB: 64-bit offsets
+    ((2, 300, 72, 8), 0, 0, 0, (0, 64, 1)),
+    ((3, 97, 136, 8), 0, ZOH, 0, (0, 32, 1)),
+    ((1, 12289, 8, 2), 0, 0, 0, (0, 64, 3)),           # 2 states: one wave covers 64 channels
+])
+def test_fwd_plan_query(lib, sizes, io, flags, conv, expect):
+    """The launch plan the forward follows (kernel, channels per workgroup,
+    segments) for shapes the GPU tests and the benchmark use, on a device
+    with 256 compute units (or none, which the query takes as 256)."""
+    from selective_state_space_10_amd import _lib
+    plan = _lib.FwdPlan()
+    assert lib.ssm_scan_fwd_plan(*sizes, io, flags, conv, ctypes.byref(plan)) == OK
+    assert (plan.kernel, plan.tile_channels, plan.segments) == expect
+    assert (plan.segment_len == 0) == (plan.segments == 1)
+    if plan.segments > 1:
+        B, L, D, N = sizes
+        assert plan.segments == -(-L // plan.segment_len)
+        assert lib.ssm_scan_fwd_workspace_bytes(*sizes, io) == 4 * B * plan.segments * D * (2 * N + 1)
+
+
+def test_fwd_plan_query_validates(lib):
+    from selective_state_space_10_amd import _lib
+    plan = _lib.FwdPlan()
+    assert lib.ssm_scan_fwd_plan(1, 0, 8, 4, 0, 0, 0, ctypes.byref(plan)) == BAD_SHAPE
+    assert lib.ssm_scan_fwd_plan(1, 16, 8, 4, 0, 16, 0, ctypes.byref(plan)) == UNSUPPORTED
+    assert lib.ssm_scan_fwd_plan(1, 16, 8, 4, 0, 0, 5, ctypes.byref(plan)) == UNSUPPORTED
+    assert lib.ssm_scan_fwd_plan(1, 16, 8, 4, 0, REV, 4, ctypes.byref(plan)) == UNSUPPORTED
+    assert lib.ssm_scan_fwd_plan(1, 16, 8, 4, 0, 0, 0, None) == NULL_ARG
 
 
 def test_option_flags_are_validated(lib):

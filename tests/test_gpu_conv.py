@@ -146,3 +146,75 @@ def test_conv_autograd(ssm):
                  C="dC", D="dD", z="dz", delta_bias="ddelta_bias", h0="dh0")
     for k, g in gname.items():
         assert nmax_err(leaves[k].grad, go[g]) <= 1e-4, k
+
+
+def _conv_slice(p, cw, cb, sel):
+    """Inputs of channels `sel` on the CPU (the convolution and the scan are
+    per channel; B and C are shared)."""
+    s = sel.to(p["u"].device)
+    return dict(x=p["u"][:, :, s].cpu(), conv_w=cw[s].cpu(), conv_b=cb[s].cpu(),
+                delta=p["delta"][:, :, s].cpu(), A=p["A"][s].cpu(), B=p["B"].cpu(),
+                C=p["C"].cpu(), D=p["D"][s].cpu(), z=p["z"][:, :, s].cpu(),
+                delta_bias=p["delta_bias"][s].cpu(), delta_softplus=True, h0=None)
+
+
+# channels at both ends of 32-channel tiles, both halves of a tile's state
+# slices, and the last channel
+_SEL_2P8B = torch.tensor([0, 1, 31, 32, 63, 64, 1999, 2048, 2559, 4095, 5088, 5119])
+
+
+def test_fwd_conv_workload2_full_size(ssm):
+    """The Mamba-2.8b layer shape (4 x 4096 x 5120, bf16) with a width-4
+    convolution, in the launch configuration the forward picks there (the
+    wave-specialised kernel on 32-channel tiles), on sampled channels."""
+    w = WORKLOADS[2]
+    p = workload_inputs(2, device="cuda")
+    cw, cb = conv_inputs(w.dim, 4, seed=2, device="cuda")
+    plan = ssm.scan_fwd_plan(w.batch, w.seqlen, w.dim, w.dstate, w.io_dtype, conv_width=4)
+    assert (plan["kernel"], plan["tile_channels"], plan["segments"]) == ("wave-specialised", 32, 1)
+    y, hf, cs = ssm.scan_fwd_conv(p["u"], cw, cb, p["delta"], p["A"], p["B"], p["C"], p["D"],
+                                  p["z"], p["delta_bias"], True, None, return_final_state=True,
+                                  save_chunk_states=True)
+    torch.cuda.synchronize()
+    sc = _SEL_2P8B.cuda()
+    y_s, hf_s, cs_s = y[:, :, sc].cpu(), hf[:, sc].cpu(), cs[:, :, :, sc].cpu()
+    ps = _conv_slice(p, cw, cb, _SEL_2P8B)
+    del y, hf, cs
+    yo, hfo, cso = oracle_c.scan_fwd_conv(**ps, chunk_len=ssm.chunk_len())
+    tol = TOL[w.io_dtype]
+    assert nmax_err(y_s, yo) <= tol
+    assert nmax_err(hf_s, hfo) <= tol
+    assert nmax_err(cs_s.permute(0, 1, 3, 2), cso) <= tol
+
+
+def test_bwd_conv_workload2_full_size(ssm):
+    """Backward of the fused convolution and scan at the Mamba-2.8b layer
+    shape.  The cotangent is zero outside the sampled channels, so dB and dC
+    (sums over channels) are sums over those channels, which the oracle
+    computes; every gradient of the other channels must be exactly zero."""
+    w = WORKLOADS[2]
+    p = workload_inputs(2, device="cuda")
+    cw, cb = conv_inputs(w.dim, 4, seed=2, device="cuda")
+    y, _, cs = ssm.scan_fwd_conv(p["u"], cw, cb, p["delta"], p["A"], p["B"], p["C"], p["D"],
+                                 p["z"], p["delta_bias"], True, None, save_chunk_states=True)
+    mask = torch.zeros(w.dim, dtype=torch.bool)
+    mask[_SEL_2P8B] = True
+    mg = mask.cuda()
+    dy = cotangent(y, 2)
+    dy[:, :, ~mg] = 0
+    del y
+    gr = ssm.scan_bwd_conv(p["u"], cw, cb, p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                           p["delta_bias"], True, None, cs, dy)
+    torch.cuda.synchronize()
+    sc = _SEL_2P8B.cuda()
+    ps = _conv_slice(p, cw, cb, _SEL_2P8B)
+    go = oracle_c.scan_bwd_conv(**ps, dy=dy[:, :, sc].cpu())
+    tol = TOL[w.io_dtype]
+    for k in ("dx", "ddelta", "dz"):
+        assert nmax_err(gr[k][:, :, sc], go[k]) <= tol, k
+        assert int(torch.count_nonzero(gr[k][:, :, ~mg])) == 0, k
+    for k in ("dB", "dC"):
+        assert nmax_err(gr[k], go[k]) <= tol, k
+    for k in ("dconv_w", "dconv_b", "dA", "dD", "ddelta_bias"):
+        assert nmax_err(gr[k][sc], go[k]) <= tol, k
+        assert int(torch.count_nonzero(gr[k][~mg])) == 0, k

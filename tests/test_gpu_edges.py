@@ -63,16 +63,45 @@ def test_more_batch_rows_than_one_grid_row_range(ssm):
     _check_bwd(ssm, p, TOL[torch.bfloat16], seed=65)
 
 
+def _assert_plan(ssm, p, tile, zoh=False, reverse=False, conv=0):
+    """The forward reaches the wave-specialised kernel on `tile`-channel tiles
+    for this problem (the launch plan the launcher itself follows)."""
+    Bsz, L, D = p["u" if "u" in p else "x"].shape
+    plan = ssm.scan_fwd_plan(Bsz, L, D, p["A"].shape[1], p["B"].dtype, zoh=zoh, reverse=reverse,
+                             per_token=p["delta"].dim() == 2, conv_width=conv)
+    assert plan == {"kernel": "wave-specialised", "tile_channels": tile, "segments": 1,
+                    "segment_len": 0}, plan
+
+
 @pytest.mark.parametrize("opts", [dict(), dict(zoh=True), dict(reverse=True, tok=True)],
                          ids=["plain", "zoh", "reverse-per-token"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_many_channel_tiles(ssm, dtype, opts):
-    """More 64-channel tiles than compute units (5 rows x 53 tiles): the
-    16-state forward switches to 32-channel tiles, the last one ragged (8 of
-    32 channels)."""
+    """More tiles than compute units even at 80 channels (8 rows x 42 tiles of
+    80 > 256): the 16-state forward takes 32-channel tiles (8 x 105, the last
+    one ragged: 8 of 32 channels), two workgroups per compute unit."""
     from tests.test_gpu_options import _check_fwd as _check_fwd_opts, _with_opts
-    p = _with_opts(_problem(5, 40, 3336, 16, dtype, seed=41, h0=True), opts.get("tok", False))
+    p = _with_opts(_problem(8, 40, 3336, 16, dtype, seed=41, h0=True), opts.get("tok", False))
+    _assert_plan(ssm, p, 32, opts.get("zoh", False), opts.get("reverse", False))
     _check_fwd_opts(ssm, p, TOL[dtype], opts.get("zoh", False), opts.get("reverse", False))
+
+
+@pytest.mark.parametrize("opts", [dict(), dict(zoh=True, tok=True)], ids=["plain", "zoh-per-token"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_many_channel_tiles_fused_conv(ssm, dtype, opts):
+    """The fused convolution on 32-channel tiles (8 x 105 tiles), against the
+    oracle's convolution followed by its scan."""
+    from tests.test_gpu_conv import _conv_problem, _gpu_fwd as _conv_fwd, _okw
+    zoh = opts.get("zoh", False)
+    p = _conv_problem(8, 40, 3336, 16, dtype, 4, seed=47, tok=opts.get("tok", False))
+    _assert_plan(ssm, p, 32, zoh=zoh, conv=4)
+    T = ssm.chunk_len()
+    y, hf, cs = _conv_fwd(ssm, _to(p, "cuda"), zoh, return_final_state=True, save_chunk_states=True)
+    torch.cuda.synchronize()
+    yo, hfo, cso = oracle_c.scan_fwd_conv(**_okw(p), chunk_len=T, zoh=zoh)
+    assert nmax_err(y, yo) <= TOL[dtype]
+    assert nmax_err(hf, hfo) <= TOL[dtype]
+    assert nmax_err(cs.permute(0, 1, 3, 2), cso) <= TOL[dtype]
 
 
 @pytest.mark.parametrize("opts", [dict(), dict(zoh=True), dict(reverse=True, tok=True)],
@@ -84,6 +113,7 @@ def test_eighty_channel_tiles(ssm, dtype, opts):
     forward takes 80-channel tiles there (on a 256-CU device)."""
     from tests.test_gpu_options import _check_fwd as _check_fwd_opts, _with_opts
     p = _with_opts(_problem(1, 37, 20480, 16, dtype, seed=43, h0=True), opts.get("tok", False))
+    _assert_plan(ssm, p, 80, opts.get("zoh", False), opts.get("reverse", False))
     _check_fwd_opts(ssm, p, TOL[dtype], opts.get("zoh", False), opts.get("reverse", False))
 
 

@@ -89,7 +89,10 @@ def test_fwd_accumulate_and_bidirectional(ssm, dtype):
     ok = _oracle_kwargs(p)
     yf, _, _ = oracle_c.scan_fwd(**ok)
     yr, _, _ = oracle_c.scan_fwd(**dict(ok, D=None), reverse=True)
-    assert nmax_err(yb, yf + yr) <= TOL[dtype] * (1 if dtype == torch.float32 else 1.5)
+    # bf16: the forward launch rounds y, the reverse launch adds to it and
+    # rounds again; emulated on the oracle's outputs that costs at most about
+    # 4e-3 of max|y| here, within the bf16 bound
+    assert nmax_err(yb, yf + yr) <= TOL[dtype]
 
 
 def test_bidirectional_sequence_split(ssm):

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 2
+#define SSM_SCAN_ABI_VERSION 3
 
 typedef enum ssm_status {
   SSM_OK = 0,
@@ -175,6 +175,28 @@ int ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, 
                     int delta_softplus, const float *h0, float *h_final, void *y,
                     float *chunk_states, void *workspace, int64_t workspace_bytes,
                     void *hip_stream, int flags);
+
+/*
+ * ssm_scan_fwd_ex without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It allocates nothing: the workspace a
+ * sequence split needs (ssm_scan_fwd_workspace_bytes) lives in a static
+ * device array of SSM_NOALLOC_SCRATCH_BYTES that the library's code object
+ * holds on every device it runs on until the process ends.  Sizes whose
+ * workspace exceeds that return SSM_ERR_WORKSPACE before anything is enqueued.
+ * The array is shared by every call on one device and keeps the last call's
+ * contents (nothing in it needs to start at zero): calls that overlap on one
+ * device (different streams, or host threads) race and must be serialised by
+ * the caller.  Arguments, outputs and errors otherwise as ssm_scan_fwd_ex;
+ * the result is identical to it.
+ */
+#define SSM_NOALLOC_SCRATCH_BYTES (16 << 20)
+
+int ssm_scan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                         const void *u, const void *delta, const float *A, const void *Bmat,
+                         const void *Cmat, const float *Dskip, const void *z,
+                         const float *delta_bias, int delta_softplus, const float *h0,
+                         float *h_final, void *y, float *chunk_states, void *hip_stream, int flags);
 
 /* Device workspace ssm_scan_bwd needs for these sizes.  -1 on invalid sizes. */
 int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,

@@ -84,6 +84,14 @@ struct FwdPlan {
 };
 FwdPlan plan_fwd(const FwdArgs &a, int io_dtype);
 
+// Bytes of the static scratch array the allocation-free forward uses in place
+// of a workspace (the largest forward workspace it accepts).
+constexpr int64_t kNoAllocScratchBytes = (int64_t)16 << 20;
+
+// Device address of that array on the current device (looked up once per
+// device; the array itself lives in scan_fwd.hip).
+hipError_t noalloc_scratch(void **ptr);
+
 int64_t fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype);
 int64_t bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype);
 int64_t bwd_conv_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype);

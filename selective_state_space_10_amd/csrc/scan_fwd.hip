@@ -33,6 +33,8 @@
 //     input are in flight while the recurrence of the current one executes.
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -961,6 +963,36 @@ static hipError_t launch_fwd_io(const FwdArgs &a, hipStream_t s) {
     case 16: return launch_fwd_t<IO, 16>(a, s);
   }
   return hipErrorInvalidValue;
+}
+
+// Scratch memory of the allocation-free forward (ssm_scan_fwd_noalloc): the
+// sequence split's per-segment states and step-size sums live here instead of
+// in a caller workspace.  One copy per device, held while the code object is
+// loaded; every call on a device shares it.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in symbol): it
+// asks the runtime for the device address once per device, below.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device (null until looked up)
+}  // namespace
+
+hipError_t noalloc_scratch(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {  // first call on this device, which is current
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 int64_t fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype) {

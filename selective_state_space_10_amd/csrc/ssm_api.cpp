@@ -167,6 +167,30 @@ int ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, 
   return hip_status(ssm::launch_fwd(a, io_dtype, (hipStream_t)hip_stream), "ssm_scan_fwd launch");
 }
 
+int ssm_scan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                         const void *u, const void *delta, const float *A, const void *Bmat,
+                         const void *Cmat, const float *Dskip, const void *z,
+                         const float *delta_bias, int delta_softplus, const float *h0,
+                         float *h_final, void *y, float *chunk_states, void *hip_stream, int flags) {
+  g_last_error[0] = 0;
+  const int st = check_sizes(batch, seqlen, dim, dstate, io_dtype);
+  if (st != SSM_OK) return st;
+  const int64_t need = ssm::fwd_workspace_bytes(batch, seqlen, dim, dstate, io_dtype);
+  if (need > ssm::kNoAllocScratchBytes)
+    return fail(SSM_ERR_WORKSPACE,
+                "these sizes need %lld bytes of scratch; the allocation-free forward holds %lld "
+                "(use ssm_scan_fwd_ex with a workspace)",
+                (long long)need, (long long)ssm::kNoAllocScratchBytes);
+  void *ws = nullptr;
+  if (need > 0) {
+    const int hs = hip_status(ssm::noalloc_scratch(&ws), "scratch address lookup");
+    if (hs != SSM_OK) return hs;
+  }
+  return ssm_scan_fwd_ex(batch, seqlen, dim, dstate, io_dtype, u, delta, A, Bmat, Cmat, Dskip, z,
+                         delta_bias, delta_softplus, h0, h_final, y, chunk_states, ws,
+                         need > 0 ? ssm::kNoAllocScratchBytes : 0, hip_stream, flags);
+}
+
 int ssm_scan_fwd_conv(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
                       const void *x, const float *conv_w, const float *conv_b, int conv_width,
                       const void *delta, const float *A, const void *Bmat, const void *Cmat,

@@ -49,7 +49,7 @@ def test_binding_signatures_match_the_header(lib):
 
 
 def test_version_and_queries(lib):
-    assert lib.ssm_abi_version() == 2
+    assert lib.ssm_abi_version() == 3
     T = lib.ssm_scan_chunk_len()
     assert T >= 16 and T & (T - 1) == 0
     assert lib.ssm_scan_chunk_states_bytes(2, T * 3 + 1, 64, 16) == 2 * 4 * 64 * 16 * 4
@@ -195,6 +195,22 @@ def test_fwd_plan_query(lib, sizes, io, flags, conv, expect):
         B, L, D, N = sizes
         assert plan.segments == -(-L // plan.segment_len)
         assert lib.ssm_scan_fwd_workspace_bytes(*sizes, io) == 4 * B * plan.segments * D * (2 * N + 1)
+
+
+def test_noalloc_forward_rejects_oversized_scratch(lib):
+    """The allocation-free forward holds a fixed scratch of 16 MiB: sizes whose
+    forward workspace is larger are refused before anything is enqueued (and
+    before the device is touched), like every other invalid argument."""
+    B, L, D, N = 1, 1 << 22, 4096, 16
+    need = lib.ssm_scan_fwd_workspace_bytes(B, L, D, N, 0)
+    assert need > 16 << 20
+    args = (B, L, D, N, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, None, None, FAKE,
+            None, None)
+    assert lib.ssm_scan_fwd_noalloc(*args, 0) == WORKSPACE
+    assert b"allocation-free" in lib.ssm_last_error()
+    assert lib.ssm_scan_fwd_noalloc(1, 0, D, N, 0, *args[5:], 0) == BAD_SHAPE
+    # within the scratch (the million-length shape needs about 2 MiB)
+    assert 0 < lib.ssm_scan_fwd_workspace_bytes(1, 1 << 20, 1024, 16, 1) <= 16 << 20
 
 
 def test_fwd_plan_query_validates(lib):

@@ -32,12 +32,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-# Vector-ALU rates of MI355X: the published fp32 vector peak, 157.3 TFLOP/s, is
-# 78.6e12 FP32 lane operations/s (an FMA counts two flops); exp2, log2 and rcp
-# run at a quarter of that rate (measured on gfx950: about 8.4 SIMD cycles per
-# wave64 v_exp_f32 against about 2 for a plain FP32 operation).
-VALU_OPS_PER_S = 157.3e12 / 2
-TRANS_OPS_PER_S = VALU_OPS_PER_S / 4
+# Nominal vector-ALU rates of MI355X: the published fp32 vector peak, 157.3
+# TFLOP/s, is 78.6e12 FP32 lane operations/s (256 CUs x 4 SIMDs x 32 lanes per
+# clock x 2.4 GHz; an FMA counts two flops), transcendentals a quarter of it.
+# The ALU floors are priced with the rates the probes measure in the same run
+# (plain v_fma_f32 and v_exp_f32, wall time, 4 waves per SIMD); these nominal
+# figures are reported beside them.
+VALU_OPS_PER_S_NOMINAL = 157.3e12 / 2
+TRANS_OPS_PER_S_NOMINAL = VALU_OPS_PER_S_NOMINAL / 4
 WORKLOAD_NAMES = ["mamba-370m-layer-fwd", "mamba-2.8b-layer-fwd", "decode-state-update",
                   "million-length-fwd", "million-length-bwd", "mamba-370m-layer-bwd",
                   "mamba-370m-layer-fwd-zoh", "mamba-370m-layer-fwd-token-delta",
@@ -62,6 +64,9 @@ def _parse():
     ap.add_argument("--rotate", type=int, default=3, help="input sets rotated between steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--alu-calibration", action="store_true",
+                    help="only time the vector-ALU probes (v_fma_f32, v_exp_f32, their 4:1 mix, "
+                         "v_mul_f32) at 1-4 waves per SIMD and print their rates")
     return ap.parse_args()
 
 
@@ -164,6 +169,137 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     torch.cuda.synchronize()
     return {"calibration": "copy", "bytes_read_per_launch": nbytes,
             "bytes_written_per_launch": nbytes, "launches": reps}
+
+
+PROBE_KINDS = {0: "v_fma_f32", 1: "v_exp_f32", 2: "1 v_exp_f32 + 4 v_fma_f32 (independent)",
+               3: "v_mul_f32", 4: "recurrence pattern (mul, exp, mul, fma, fma)"}
+
+
+def _probe_lib():
+    import ctypes
+
+    from selective_state_space_10_amd import build as b
+    if not os.path.exists(b.PROBE_LIB):
+        raise ImportError(f"{b.PROBE_LIB} is missing (build the package first)")
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    lib.ssm_probe_valu.restype = ctypes.c_int
+    lib.ssm_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.POINTER(ctypes.c_int), ctypes.c_void_p]
+    lib.ssm_probe_instructions_per_lane.restype = ctypes.c_int64
+    lib.ssm_probe_instructions_per_lane.argtypes = [ctypes.c_int, ctypes.c_int64]
+    lib.ssm_probe_wave_placement.restype = ctypes.c_int
+    lib.ssm_probe_wave_placement.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    return lib
+
+
+def _probe_rate(lib, kind, W, iters, reps):
+    """Lane operations per second of probe ``kind`` at W waves per SIMD: the
+    median HIP-event time of ``reps`` launches after one untimed launch."""
+    import ctypes
+    import statistics
+
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(cus * 1024, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    wgs = ctypes.c_int(0)
+    times = []
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st = lib.ssm_probe_valu(kind, W, iters, out.data_ptr(), out.numel(), ctypes.byref(wgs),
+                                ctypes.c_void_p(stream.cuda_stream))
+        e1.record(stream)
+        if st != 0:
+            raise RuntimeError(f"probe launch failed with status {st}")
+        torch.cuda.synchronize()
+        if r:  # the first launch loads the code object
+            times.append(e0.elapsed_time(e1) * 1e-3)
+    t = statistics.median(times)
+    per_lane = lib.ssm_probe_instructions_per_lane(kind, iters)
+    return wgs.value * 256 * W * per_lane / t, t, per_lane * W
+
+
+_RATES = {}
+
+
+def _measured_alu_rates():
+    """Plain FP32 (v_fma_f32) and transcendental (v_exp_f32) lane-operation
+    rates measured now by the probes at 4 waves per SIMD (about 20 ms)."""
+    if not _RATES:
+        lib = _probe_lib()
+        _RATES["plain"] = _probe_rate(lib, 0, 4, 10000, 3)[0]
+        _RATES["trans"] = _probe_rate(lib, 1, 4, 4000, 3)[0]
+    return _RATES["plain"], _RATES["trans"]
+
+
+def _alu_block(kind, upd, td, per_upd, per_td, ms_launch):
+    """A vector-ALU floor: ``per_upd`` = (plain, transcendental) instructions per
+    state update, ``per_td`` the same per (b,t,d), priced at the measured rates
+    (each class at its own peak, so the floor is a lower bound of the time)."""
+    plain, trans = _measured_alu_rates()
+    floor_s = (upd * (per_upd[0] / plain + per_upd[1] / trans)
+               + td * (per_td[0] / plain + per_td[1] / trans))
+    nominal_s = (upd * (per_upd[0] / VALU_OPS_PER_S_NOMINAL + per_upd[1] / TRANS_OPS_PER_S_NOMINAL)
+                 + td * (per_td[0] / VALU_OPS_PER_S_NOMINAL + per_td[1] / TRANS_OPS_PER_S_NOMINAL))
+    achieved = upd / (ms_launch * 1e-3) / 1e9
+    peak = upd / floor_s / 1e9
+    return {"kind": kind, "achieved": achieved, "peak": peak, "unit": "Gupdates/s",
+            "frac": achieved / peak, "floor_ms": floor_s * 1e3,
+            "rates": {"plain_lane_ops_per_s": plain, "trans_lane_ops_per_s": trans,
+                      "source": "measured in this run: v_fma_f32 and v_exp_f32 probes "
+                                "(libssm_alu_probe.so), one workgroup per CU, 4 waves per SIMD, "
+                                "HIP-event wall time"},
+            "nominal": {"plain_lane_ops_per_s": VALU_OPS_PER_S_NOMINAL,
+                        "trans_lane_ops_per_s": TRANS_OPS_PER_S_NOMINAL,
+                        "floor_ms": nominal_s * 1e3, "frac": nominal_s * 1e3 / ms_launch}}
+
+
+def alu_calibration(reps=5):
+    """Wall-time rates of the vector-ALU probes (libssm_alu_probe.so): one
+    workgroup per compute unit, W = 1..4 waves per SIMD, each launch timed with
+    HIP events on the stream it runs on; the median of ``reps`` launches."""
+    import ctypes
+
+    import torch
+    lib = _probe_lib()
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    stream = torch.cuda.current_stream()
+    rows = []
+    for kind, name in PROBE_KINDS.items():
+        iters = 2000 if kind in (2, 4) else 4000 if kind == 1 else 10000
+        for W in (1, 2, 3, 4):
+            rate, t, wave_instr_per_simd = _probe_rate(lib, kind, W, iters, reps)
+            rows.append({"kind": name, "waves_per_simd": W, "seconds": t,
+                         "lane_ops_per_s": rate,
+                         "ns_per_wave_instruction_per_simd": t * 1e9 / wave_instr_per_simd,
+                         "cycles_at_2p4ghz": t * 2.4e9 / wave_instr_per_simd})
+    # where the waves of the scan's workgroup shapes land: SIMD of each wave
+    placement = []
+    for threads, lds in ((768, 86016), (960, 106496), (384, 43008), (512, 126976), (768, 0)):
+        nw = threads // 64
+        buf = torch.full((cus * nw,), -1, dtype=torch.int32, device="cuda")
+        st = lib.ssm_probe_wave_placement(threads, lds, cus, buf.data_ptr(), buf.numel(),
+                                          ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"placement probe failed with status {st}")
+        torch.cuda.synchronize()
+        simd = (buf.view(cus, nw) & 3).cpu()
+        patterns = {}
+        for row in simd.tolist():
+            patterns[tuple(row)] = patterns.get(tuple(row), 0) + 1
+        common = sorted(patterns.items(), key=lambda kv: -kv[1])[:3]
+        placement.append({"threads": threads, "lds_bytes": lds,
+                          "simd_of_wave_most_common": [list(k) for k, _ in common],
+                          "workgroups_with_that_pattern": [v for _, v in common],
+                          "waves_per_simd_max": int(max(torch.bincount(r, minlength=4).max()
+                                                        for r in simd))})
+    return {"calibration": "valu", "device": props.name, "cus": cus, "placement": placement,
+            "method": "one workgroup per CU, W waves per SIMD, 8 independent chains per lane, "
+                      "HIP-event wall time of one launch (median of 5 after one untimed)",
+            "rows": rows}
 
 
 def _r3w1_ceiling(sets, steps):
@@ -275,16 +411,9 @@ def _alu_floor(Bsz, L, D, N, ms_launch):
     by the N states, 10 FP32 operations (step size and softplus 4, SiLU 2, dt*u,
     D*u, the skip add, the gate) and 4 transcendentals (softplus: exp2, log2;
     SiLU: exp2, rcp)."""
-    upd, td = Bsz * L * D * N, Bsz * L * D
-    floor_s = (upd * (4 / VALU_OPS_PER_S + 1 / TRANS_OPS_PER_S)
-               + td * (10 / VALU_OPS_PER_S + 4 / TRANS_OPS_PER_S))
-    achieved = upd / (ms_launch * 1e-3) / 1e9
-    peak = upd / floor_s / 1e9
-    return {"kind": "vector-ALU floor of the plain forward (4 FP32 ops + 1 exp2 per state update, "
-                    "10 FP32 ops + 4 transcendentals per (b,t,d)) at the published fp32 vector rate, "
-                    "transcendentals at a quarter of it",
-            "achieved": achieved, "peak": peak, "unit": "Gupdates/s", "frac": achieved / peak,
-            "floor_ms": floor_s * 1e3}
+    return _alu_block("vector-ALU floor of the plain forward (4 FP32 ops + 1 exp2 per state update, "
+                      "10 FP32 ops + 4 transcendentals per (b,t,d)), each class at its measured rate",
+                      Bsz * L * D * N, Bsz * L * D, (4, 1), (10, 4), ms_launch)
 
 
 def bench_decode(args, zoh=False):
@@ -338,16 +467,9 @@ def _alu_floor_bwd(Bsz, L, D, N, ms_launch):
     sigma(s), sigma(z) for the gate and its derivative, the input gradients
     du, ddelta, dz, and the dD and dbias sums).  A sequence split's first pass
     is extra work the floor does not count."""
-    upd, td = Bsz * L * D * N, Bsz * L * D
-    floor_s = (upd * (14 / VALU_OPS_PER_S + 1 / TRANS_OPS_PER_S)
-               + td * (24 / VALU_OPS_PER_S + 6 / TRANS_OPS_PER_S))
-    achieved = upd / (ms_launch * 1e-3) / 1e9
-    peak = upd / floor_s / 1e9
-    return {"kind": "vector-ALU floor of the backward (14 FP32 ops + 1 exp2 per state update, "
-                    "24 FP32 ops + 6 transcendentals per (b,t,d)) at the published fp32 vector rate, "
-                    "transcendentals at a quarter of it",
-            "achieved": achieved, "peak": peak, "unit": "Gupdates/s", "frac": achieved / peak,
-            "floor_ms": floor_s * 1e3}
+    return _alu_block("vector-ALU floor of the backward (14 FP32 ops + 1 exp2 per state update, "
+                      "24 FP32 ops + 6 transcendentals per (b,t,d)), each class at its measured rate",
+                      Bsz * L * D * N, Bsz * L * D, (14, 1), (24, 6), ms_launch)
 
 
 def bench_bwd(args, idx, name, conv=0, zoh=False):
@@ -413,6 +535,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         print(json.dumps(copy_calibration()), flush=True)
+        return
+    if args.alu_calibration:
+        print(json.dumps(alu_calibration()), flush=True)
         return
     import selective_state_space_10_amd as m
     m.load()

@@ -38,6 +38,30 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_probe_library_exports_its_header():
+    """The vector-ALU probe library (a measurement tool the benchmark loads)
+    exports exactly what include/ssm_alu_probe.h declares, and refuses bad
+    arguments without a device."""
+    from selective_state_space_10_amd import build
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "ssm_alu_probe.h")).read(),
+                  flags=re.S)
+    names = sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["ssm_probe_instructions_per_lane", "ssm_probe_valu", "ssm_probe_wave_placement"]
+    probe = ctypes.CDLL(build.PROBE_LIB)
+    for n in names:
+        assert hasattr(probe, n), n
+    probe.ssm_probe_instructions_per_lane.restype = ctypes.c_int64
+    probe.ssm_probe_instructions_per_lane.argtypes = [ctypes.c_int, ctypes.c_int64]
+    assert probe.ssm_probe_instructions_per_lane(0, 10) == 10 * 64
+    assert probe.ssm_probe_instructions_per_lane(2, 10) == 10 * 64 * 5
+    probe.ssm_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    wg = ctypes.c_int(0)
+    assert probe.ssm_probe_valu(0, 5, 10, FAKE, 1 << 20, ctypes.addressof(wg), None) == 1
+    assert probe.ssm_probe_valu(5, 1, 10, FAKE, 1 << 20, ctypes.addressof(wg), None) == 1
+    assert probe.ssm_probe_valu(0, 1, 10, None, 1 << 20, ctypes.addressof(wg), None) == 1
+
+
 def test_binding_signatures_match_the_header(lib):
     """Each ctypes prototype has as many arguments as the header declares."""
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)

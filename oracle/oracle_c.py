@@ -31,6 +31,20 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def build_sanitized(path: str) -> str:
+    """Compile the oracle with AddressSanitizer and UndefinedBehaviorSanitizer
+    (any undefined-behaviour report aborts) into ``path``, for a test run of the
+    oracle's checks against it (load it with ORACLE_LIB_OVERRIDE=path and the
+    ASan runtime preloaded).  Same floating-point flags as build()."""
+    tmp = path + ".tmp"
+    subprocess.check_call(["gcc", "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                           "-fno-fast-math", "-Wall", "-fno-omit-frame-pointer",
+                           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                           "-o", tmp, _SRC, "-lm", "-lpthread"])
+    os.replace(tmp, path)
+    return path
+
+
 def _load():
     global _lib
     if _lib is None:

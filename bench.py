@@ -78,18 +78,26 @@ def _source_sha(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel_key: str, sha: str, launches_per_step: int = 1):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+# sources whose hash identifies the kernels of each kind of line
+SHA_FILES = {"fwd": ("scan_fwd.hip", "device_common.hpp", "kernels.hpp"),
+             "bwd": ("scan_bwd.hip", "device_common.hpp", "kernels.hpp"),
+             "decode": ("state_update.hip", "device_common.hpp", "kernels.hpp")}
+
+
+def _traffic(workload: str, sha: str):
+    """HBM bytes per step (all launches of the step: FETCH_SIZE and WRITE_SIZE
+    scaled by a plain copy's counters) from the committed rocprofv3 summary
+    profiles/hbm_traffic.json, if it was taken on the current kernel source;
+    else None."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
-            rec = json.load(f).get(kernel_key)
+            rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
     if not rec or rec.get("source_sha") != sha:
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("bytes_per_step")
 
 
 PREWARM_S = 0.25  # untimed seconds of the same step before the warmup steps
@@ -136,25 +144,162 @@ def _time_launches(fn, steps, warmup, rotate_inputs):
     return start.elapsed_time(stop) / steps, sum(per) / len(per), wall
 
 
-def _cpu_baseline_fwd(p_cpu, min_seconds=10.0):
-    """The fp64 C oracle's forward over the same inputs, on all host cores it may
-    use, repeated until at least ``min_seconds`` of wall time have passed."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# oracle work per timed sample: about a second on all host cores, and about a
+# second on one core for the single-thread sample (state updates)
+_CPU_UPDATES_MULTI = 2e9
+_CPU_UPDATES_SINGLE = 1e8
+
+
+def _channel_block(D, per_channel_updates, budget):
+    """Channels [0, n) of a sample of about ``budget`` state updates (a multiple
+    of 8, at least 8, at most D)."""
+    n = int(budget // per_channel_updates) // 8 * 8
+    return max(8, min(D, n))
+
+
+def _slice_ch(p, n):
+    """CPU fp64-ready copies of a workload's tensors restricted to channels [0, n)."""
+    import torch
+    out = {}
+    for k, v in p.items():
+        if not isinstance(v, torch.Tensor):
+            out[k] = v
+        elif k in ("u", "z", "dy", "x") or (k == "delta" and v.dim() == 3):
+            out[k] = v[..., :n].cpu()
+        elif k in ("A", "D", "delta_bias", "conv_w", "conv_b"):
+            out[k] = v[:n].cpu()
+        else:  # B, C (shared by the channels), a per-token delta
+            out[k] = v.cpu()
+    return out
+
+
+def _cpu_baseline(runs, units_of, describe, repeats=3):
+    """The fp64 C oracle as it stands, timed on the host: ``runs`` maps a
+    thread count to a callable running one sample (the same work for every
+    count), ``units_of`` maps it to the sample's tokens*channels.  Reports the
+    median of ``repeats`` runs on all usable cores (the value) and on one."""
+    import statistics
     from oracle import oracle_c
     threads = oracle_c.default_threads()
-    kw = {k: p_cpu[k] for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
-    conv = {k: oracle_c._f64(v) for k, v in kw.items()}
-    reps, total = 0, 0.0
-    while total < min_seconds:
-        t0 = time.perf_counter()
-        oracle_c.scan_fwd(**conv, delta_softplus=True, nthreads=threads)
-        total += time.perf_counter() - t0
-        reps += 1
-    Bsz, L, D = p_cpu["u"].shape
-    N = p_cpu["A"].shape[1]
-    return {"value": reps * Bsz * L * D / total, "unit": UNIT, "cores": threads, "kind": "oracle",
-            "sample": f"{reps} full forward steps of the same workload ({Bsz}x{L}x{D}x{N}, "
-                      f"fp64 C oracle, inputs upcast from the fp32 draws), {total:.1f} s wall",
-            "seconds": round(total, 3)}
+    res = {}
+    for nthr in sorted({threads, 1}, reverse=True):
+        fn = runs(nthr)
+        ts = []
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        res[nthr] = (statistics.median(ts), ts, units_of(nthr))
+    t, ts, units = res[threads]
+    out = {"value": units / t, "unit": UNIT, "cores": threads, "kind": "oracle",
+           "sample": describe(threads), "statistic": f"median of {repeats}",
+           "seconds": round(sum(ts), 3), "cpu_model": _cpu_model()}
+    t1, ts1, units1 = res[1]
+    out["single_thread"] = {"value": units1 / t1, "unit": UNIT, "cores": 1,
+                            "sample": describe(1), "statistic": f"median of {repeats}",
+                            "seconds": round(sum(ts1), 3)}
+    return out
+
+
+def _cpu_baseline_fwd(p, Bsz, L, D, N, zoh=False, bidirectional=False, conv=0, repeats=3):
+    """Forward oracle (with the line's options) on channel blocks of the
+    workload's own inputs: the whole workload where it fits the multi-core
+    budget, a block of channels for the single-core sample."""
+    from oracle import oracle_c
+    nch = {0: _channel_block(D, Bsz * L * N, _CPU_UPDATES_MULTI),
+           1: _channel_block(D, Bsz * L * N, _CPU_UPDATES_SINGLE)}
+    samples = {}
+
+    def runs(nthr):
+        n = nch[1] if nthr == 1 else nch[0]
+        if n not in samples:
+            samples[n] = {k: oracle_c._f64(v) if hasattr(v, "dim") else v
+                          for k, v in _slice_ch(p, n).items()}
+        q = samples[n]
+        kw = {k: q.get(k) for k in ("delta", "A", "B", "C", "D", "z", "delta_bias")}
+        if conv:
+            return lambda: oracle_c.scan_fwd_conv(q["u"], q["conv_w"], q["conv_b"], **kw,
+                                                  delta_softplus=True, nthreads=nthr, zoh=zoh)
+        if bidirectional:
+            def both():
+                oracle_c.scan_fwd(q["u"], **kw, delta_softplus=True, nthreads=nthr, zoh=zoh)
+                oracle_c.scan_fwd(q["u"], **dict(kw, D=None), delta_softplus=True, nthreads=nthr,
+                                  zoh=zoh, reverse=True)
+            return both
+        return lambda: oracle_c.scan_fwd(q["u"], **kw, delta_softplus=True, nthreads=nthr, zoh=zoh)
+
+    def units(nthr):
+        return Bsz * L * (nch[1] if nthr == 1 else nch[0])
+
+    def describe(nthr):
+        n = nch[1] if nthr == 1 else nch[0]
+        what = "the whole workload" if n == D else f"channels 0..{n - 1} of {D}"
+        return (f"fp64 C oracle forward over {what} ({Bsz}x{L}x{n}x{N}, the workload's own inputs "
+                f"upcast to fp64), {nthr} thread(s)")
+    return _cpu_baseline(runs, units, describe, repeats)
+
+
+def _cpu_baseline_bwd(p, dy, Bsz, L, D, N, zoh=False, conv=0, repeats=3):
+    """Backward oracle (recomputing its forward) on channel blocks; its sums
+    over channels (dB, dC) cover the block only, which does not change the
+    work per token and channel."""
+    from oracle import oracle_c
+    nch = {0: _channel_block(D, 3 * Bsz * L * N, _CPU_UPDATES_MULTI),
+           1: _channel_block(D, 3 * Bsz * L * N, _CPU_UPDATES_SINGLE)}
+    samples = {}
+
+    def runs(nthr):
+        n = nch[1] if nthr == 1 else nch[0]
+        if n not in samples:
+            samples[n] = {k: oracle_c._f64(v) if hasattr(v, "dim") else v
+                          for k, v in _slice_ch(dict(p, dy=dy), n).items()}
+        q = samples[n]
+        kw = {k: q.get(k) for k in ("delta", "A", "B", "C", "D", "z", "delta_bias")}
+        if conv:
+            return lambda: oracle_c.scan_bwd_conv(q["u"], q["conv_w"], q["conv_b"], **kw,
+                                                  delta_softplus=True, dy=q["dy"], nthreads=nthr,
+                                                  zoh=zoh)
+        return lambda: oracle_c.scan_bwd(q["u"], **kw, delta_softplus=True, dy=q["dy"],
+                                         nthreads=nthr, zoh=zoh)
+
+    def units(nthr):
+        return Bsz * L * (nch[1] if nthr == 1 else nch[0])
+
+    def describe(nthr):
+        n = nch[1] if nthr == 1 else nch[0]
+        what = "the whole workload" if n == D else f"channels 0..{n - 1} of {D}"
+        return (f"fp64 C oracle backward (with its own forward recompute) over {what} "
+                f"({Bsz}x{L}x{n}x{N}), {nthr} thread(s)")
+    return _cpu_baseline(runs, units, describe, repeats)
+
+
+def _cpu_baseline_decode(d, Bsz, D, N, zoh=False, repeats=3):
+    """Decode oracle (single-threaded as written): one step of the whole
+    (B, D, N) state, repeated; the all-core figure is the same run."""
+    from oracle import oracle_c
+    q = {k: (oracle_c._f64(v.cpu()) if hasattr(v, "dim") else v) for k, v in d.items()}
+
+    def runs(nthr):
+        return lambda: oracle_c.state_update(q["state"], q["u"][0], q["delta"][0], q["A"],
+                                             q["B"][0], q["C"][0], q["D"], q["z"][0],
+                                             q["delta_bias"], True, zoh=zoh)
+    out = _cpu_baseline(runs, lambda nthr: Bsz * D,
+                        lambda nthr: f"fp64 C oracle state update, one step of the whole "
+                                     f"{Bsz}x{D}x{N} state (the oracle is single-threaded)",
+                        repeats)
+    out["cores"] = 1
+    return out
 
 
 def copy_calibration(nbytes=1 << 30, reps=5):
@@ -364,8 +509,8 @@ def bench_fwd(args, idx, name, zoh=False, per_token=False, bidirectional=False, 
     if conv:  # x replaces u; taps and bias are read once
         nbytes += D * (conv + 1) * 4
     achieved = nbytes / (ms_launch * 1e-3) / 1e9
-    sha = _source_sha("scan_fwd.hip", "device_common.hpp", "kernels.hpp")
-    traffic = _traffic(f"fwd:{name}", sha)
+    sha = _source_sha(*SHA_FILES["fwd"])
+    traffic = _traffic(name, sha)
     line = {
         "metric": (METRIC if idx == 1 and name == "mamba-370m-layer-fwd"
                    else f"selective-scan fwd tokens*channels/s, {name}"),
@@ -383,7 +528,7 @@ def bench_fwd(args, idx, name, zoh=False, per_token=False, bidirectional=False, 
                                "bidirectional": bidirectional, "conv_width": conv}},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic if not (zoh or per_token or bidirectional or conv) else None,
+                     "traffic": traffic,
                      "algorithmic_bytes": nbytes,
                      "kernel_ms": ms_launch, "source_sha": sha},
     }
@@ -396,10 +541,10 @@ def bench_fwd(args, idx, name, zoh=False, per_token=False, bidirectional=False, 
         ceil = _r3w1_ceiling(sets, max(args.steps, 10))
         ceil["frac"] = achieved / ceil["achieved"]  # the scan's rate over the measured ceiling
         line["roofline"]["ceiling"] = ceil
-    if not args.no_cpu_baseline and name == "mamba-370m-layer-fwd":
-        pc = workload_inputs(idx, device="cuda", seed=idx)
-        pc = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in pc.items()}
-        line["cpu_baseline"] = _cpu_baseline_fwd(pc)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = _cpu_baseline_fwd(sets[0], Bsz, L, D, N, zoh=zoh,
+                                                 bidirectional=bidirectional, conv=conv,
+                                                 repeats=1 if idx == 4 else 3)
     if name == "mamba-370m-layer-fwd":
         line["context"] = PAGES_CLAIM
     return line
@@ -441,7 +586,10 @@ def bench_decode(args, zoh=False):
                        d["z"][t], d["delta_bias"], True, zoh=zoh)
 
     _, ms_one, _ = _time_launches(step_one, w.steps, args.warmup, tok)
-    return {"metric": "decode state update tokens*channels/s", "unit": UNIT,
+    extra = {}
+    if not args.no_cpu_baseline:
+        extra["cpu_baseline"] = _cpu_baseline_decode(d, w.batch, w.dim, w.dstate, zoh=zoh)
+    return {**extra, "metric": "decode state update tokens*channels/s", "unit": UNIT,
             "value": w.batch * w.dim / (ms_step * 1e-3), "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16 storage, f32 compute",
@@ -450,7 +598,9 @@ def bench_decode(args, zoh=False):
                                             "prewarm_steps": prewarm,
                                             "options": {"zoh": zoh}},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": _traffic("decode-state-update" + ("-zoh" if zoh else ""),
+                                             _source_sha(*SHA_FILES["decode"])),
                          "algorithmic_bytes": nbytes, "kernel_ms": ms_launch,
                          "mall_resident": {"kind": "one state buffer, 64 consecutive steps",
                                            "achieved": nbytes / (ms_one * 1e-3) / 1e9,
@@ -479,7 +629,7 @@ def bench_bwd(args, idx, name, conv=0, zoh=False):
     import torch
 
     import selective_state_space_10_amd as m
-    from workloads import WORKLOADS, cotangent, workload_inputs
+    from workloads import WORKLOADS, algorithmic_bytes_bwd, cotangent, workload_inputs
     w = WORKLOADS[idx]
     p = workload_inputs(idx, device="cuda")
     if conv:
@@ -506,10 +656,15 @@ def bench_bwd(args, idx, name, conv=0, zoh=False):
     io = 4 if w.io_dtype == torch.float32 else 2
     # u, delta, z, dy in; du, ddelta, dz out; B, C in and dB, dC out; chunk states in; A, D,
     # bias in and dA, dD, dbias out
-    nbytes = (7 * Bsz * L * D * io + 4 * Bsz * L * N * io + cs.numel() * 4
-              + D * N * 4 * 2 + D * 4 * 4)
+    nbytes = algorithmic_bytes_bwd(Bsz, L, D, N, io, m.chunk_len())
+    assert cs.numel() * 4 == Bsz * -(-L // m.chunk_len()) * N * D * 4
     achieved = nbytes / (ms_launch * 1e-3) / 1e9
-    return {"metric": f"selective-scan bwd tokens*channels/s, {name}", "unit": UNIT,
+    extra = {}
+    if not args.no_cpu_baseline:
+        pb = dict(p, conv_w=cw, conv_b=cb) if conv else p
+        extra["cpu_baseline"] = _cpu_baseline_bwd(pb, dy, Bsz, L, D, N, zoh=zoh, conv=conv,
+                                                  repeats=1 if idx == 4 else 3)
+    return {**extra, "metric": f"selective-scan bwd tokens*channels/s, {name}", "unit": UNIT,
             "value": Bsz * L * D / (ms_step * 1e-3), "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None,
@@ -518,7 +673,8 @@ def bench_bwd(args, idx, name, conv=0, zoh=False):
                                             "seqlen": L, "dim": D, "dstate": N,
                                             "prewarm_steps": _time_launches.prewarm_steps},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": _traffic(name, _source_sha(*SHA_FILES["bwd"])),
                          "algorithmic_bytes": nbytes, "kernel_ms": ms_launch,
                          **({} if conv or zoh else {"alu": _alu_floor_bwd(Bsz, L, D, N, ms_launch)})}}
 

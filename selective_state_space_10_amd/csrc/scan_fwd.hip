@@ -40,6 +40,9 @@
 
 namespace ssm {
 
+// XCDs of an MI355X (gfx950): workgroups are handed to them in turn.
+constexpr int64_t kXcds = 8;
+
 // MODE 0: full forward (y, chunk states, final state).  MODE 1: first phase of
 // a sequence split: the segment's end state from a zero start, and the sum of
 // its step sizes (no y).  blockIdx.z is the segment.
@@ -398,8 +401,22 @@ fwd_ws_kernel(FwdArgs a) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t L = a.L, D = a.D;
-  const int64_t b = blockIdx.y;
-  const int64_t d0 = (int64_t)blockIdx.x * CPW;
+  // Workgroups are handed to the XCDs in turn (workgroup i to XCD i mod 8) and
+  // every XCD has its own L2.  Neighbouring tiles share the cache lines at
+  // their edges (a row of 80 bf16 channels is 160 bytes), so the (tile, batch
+  // row) pairs of an unsplit grid are renumbered to give every XCD one
+  // contiguous run of them, and a line shared by two tiles is fetched once.
+  int64_t tile = blockIdx.x, b = blockIdx.y;
+  if (gridDim.z == 1) {
+    const int64_t P = (int64_t)gridDim.x * gridDim.y;
+    if (P % kXcds == 0) {
+      const int64_t lin = blockIdx.x + (int64_t)blockIdx.y * gridDim.x;
+      const int64_t r = (lin % kXcds) * (P / kXcds) + lin / kXcds;
+      tile = r % gridDim.x;
+      b = r / gridDim.x;
+    }
+  }
+  const int64_t d0 = tile * CPW;
   const int64_t row0 = b * L;
   // With a sequence split, workgroup z scans segment z from its composed
   // start state; steps are counted from the segment's first step tb.

@@ -187,3 +187,12 @@ def algorithmic_bytes_decode(batch, dim, dstate, io_bytes):
     bd = batch * dim
     return (2 * bd * dstate * 4 + 3 * bd * io_bytes + 2 * batch * dstate * io_bytes
             + dim * dstate * 4 + 2 * dim * 4 + bd * io_bytes)
+
+
+def algorithmic_bytes_bwd(batch, seqlen, dim, dstate, io_bytes, chunk_len=32):
+    """Bytes a backward must move: u, delta, z, dy in and du, ddelta, dz out
+    (B,L,D); B, C in and dB, dC out (B,L,N); the chunk-boundary states in; A,
+    D, bias in and dA, dD, dbias out."""
+    K = -(-seqlen // chunk_len)
+    return (7 * batch * seqlen * dim * io_bytes + 4 * batch * seqlen * dstate * io_bytes
+            + batch * K * dstate * dim * 4 + dim * dstate * 4 * 2 + dim * 4 * 4)

@@ -290,6 +290,29 @@ int ssm_scan_bwd_conv(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate
                       int64_t workspace_bytes, void *hip_stream, int flags);
 
 /*
+ * Scan of affine maps along rows (fp32, row-major (rows, len), device memory):
+ *   s = h0[r] (0 if h0 is NULL); for i in scan order: s = a[r,i] * s + b[r,i];
+ *   h[r,i] = s.
+ * Scan order is i = 0 .. len-1, or len-1 .. 0 if reverse = 1.  Every step of
+ * the recurrence is such a map (reading guide, "Yöntem": the new state is the
+ * discretised A times the old state plus the discretised input), and because
+ * the maps compose associatively -- (a1, b1) then (a2, b2) is (a1 a2,
+ * a2 b1 + b2) -- the scan runs in parallel: one wave per row, 64 positions at
+ * a time with a wave-wide associative scan (DPP cross-lane moves), the state
+ * carried between pieces.  The library folds the segments of a split sequence
+ * with the same primitive; this entry point exposes it, for example to fold
+ * the segment aggregates of a sequence sharded over several devices.  Results
+ * equal the sequential loop up to the rounding of the different association
+ * (exactly, when every product and sum is exact in fp32).
+ * Pointers need 4-byte alignment; h may be the same array as a or b.  Errors:
+ * rows or len < 1 (SSM_ERR_BAD_SHAPE), rows > 4 * (2^31 - 1) or reverse not 0
+ * or 1 (SSM_ERR_UNSUPPORTED), a, b or h NULL (SSM_ERR_NULL_ARG); nothing is
+ * enqueued on error.
+ */
+int ssm_affine_scan(int64_t rows, int64_t len, const float *a, const float *b, const float *h0,
+                    float *h, int reverse, void *hip_stream);
+
+/*
  * One decode step (reading guide, "Sorular", the question on KV caches: the
  * model keeps a fixed D x N state per layer and advances it one token at a
  * time).  state (B,D,N) fp32 is read once and overwritten in place with the

@@ -70,6 +70,8 @@ def _load():
         lib.oracle_conv1d_silu.restype = CI
         lib.oracle_conv1d_silu_bwd.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
         lib.oracle_conv1d_silu_bwd.restype = CI
+        lib.oracle_affine_scan.argtypes = [I, I, P, P, P, P, CI]
+        lib.oracle_affine_scan.restype = CI
         for f in ("oracle_softplus", "oracle_sigmoid", "oracle_silu"):
             getattr(lib, f).argtypes = [ctypes.c_double]
             getattr(lib, f).restype = ctypes.c_double
@@ -174,6 +176,23 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delt
     if rc != 0:
         raise ValueError(f"oracle_state_update failed ({rc})")
     return st, y
+
+
+def affine_scan(a, b, h0=None, reverse=False):
+    """Sequential fold of h -> a h + b along the last axis from h0 (zeros if
+    None); returns every state, fp64, a's shape."""
+    a, b, h0 = _f64(a), _f64(b), _f64(h0)
+    if a.shape != b.shape or a.ndim < 1:
+        raise ValueError("a and b must have one shape")
+    length = a.shape[-1]
+    rows = a.size // length
+    h = np.empty_like(a)
+    if h0 is not None and h0.size != rows:
+        raise ValueError("h0 must hold one state per row")
+    rc = _load().oracle_affine_scan(rows, length, _p(a), _p(b), _p(h0), _p(h), int(bool(reverse)))
+    if rc != 0:
+        raise ValueError(f"oracle_affine_scan failed ({rc})")
+    return h
 
 
 def conv1d_silu(x, w, bias=None):

@@ -490,3 +490,24 @@ int oracle_conv1d_silu_bwd(int64_t B, int64_t L, int64_t D, int64_t K, const dou
   free(g);
   return 0;
 }
+
+/* ---- scan of affine maps ------------------------------------------------ */
+
+/* The sequential fold of the maps h -> a h + b along each row of row-major
+ * (rows, len) arrays: s = h0[r] (0 if h0 is NULL), then for i in scan order
+ * (0 .. len-1, or len-1 .. 0 if reverse) s = a[r,i] * s + b[r,i] and
+ * h[r,i] = s.  One step of the recurrence above is such a map (reading guide,
+ * "Yöntem": the new state is Abar times the old one plus the input term). */
+int oracle_affine_scan(int64_t rows, int64_t len, const double *a, const double *b,
+                       const double *h0, double *h, int reverse) {
+  if (rows < 1 || len < 1) return -1;
+  for (int64_t r = 0; r < rows; ++r) {
+    double s = h0 ? h0[r] : 0.0;
+    for (int64_t k = 0; k < len; ++k) {
+      const int64_t i = r * len + (reverse ? len - 1 - k : k);
+      s = a[i] * s + b[i];
+      h[i] = s;
+    }
+  }
+  return 0;
+}

@@ -15,7 +15,7 @@ EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_error", "ssm_scan_c
            "ssm_scan_fwd_ex", "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_ex",
            "ssm_state_update", "ssm_state_update_ex", "ssm_scan_fwd_conv",
            "ssm_scan_bwd_conv_workspace_bytes", "ssm_scan_bwd_conv", "ssm_scan_fwd_plan",
-           "ssm_scan_fwd_noalloc")
+           "ssm_scan_fwd_noalloc", "ssm_affine_scan")
 
 
 class FwdPlan(ctypes.Structure):
@@ -83,6 +83,8 @@ def load() -> ctypes.CDLL:
     # ddelta_bias, dh0, workspace
     lib.ssm_scan_bwd_conv.argtypes = [I64] * 4 + [INT] + [P] * 3 + [INT] + [P] * 7 + [INT] \
         + [P] * 16 + [I64, P, INT]
+    lib.ssm_affine_scan.restype = INT
+    lib.ssm_affine_scan.argtypes = [I64, I64, P, P, P, P, INT, P]
     lib.ssm_scan_fwd_noalloc.restype = INT
     lib.ssm_scan_fwd_noalloc.argtypes = [I64] * 4 + [INT] + [P] * 8 + [INT] + [P] * 5 + [INT]
     lib.ssm_scan_fwd_plan.restype = INT

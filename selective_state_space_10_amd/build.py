@@ -15,7 +15,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libssm_scan.so")
 ARCH = "gfx950"
 
-SOURCES = ["ssm_api.cpp", "scan_fwd.hip", "scan_bwd.hip", "state_update.hip"]
+SOURCES = ["ssm_api.cpp", "scan_fwd.hip", "scan_bwd.hip", "state_update.hip", "affine_scan.hip"]
 # the vector-ALU rate probes (a measurement tool beside the library)
 PROBE_SOURCES = ["alu_probe.hip"]
 PROBE_LIB = os.path.join(HERE, "libssm_alu_probe.so")

@@ -140,6 +140,44 @@ __device__ __forceinline__ float step_size(float raw, float bias, bool softplus)
   return softplus ? softplus_f(s) : s;
 }
 
+// ---- wave-wide associative scan of affine maps
+//
+// A step of the recurrence, h -> a h + b, is an affine map; applying (a1, b1)
+// and then (a2, b2) gives (a1 a2, a2 b1 + b2), an associative composition with
+// identity (1, 0) (the same algebra that lets the scan be split over time and
+// recombined).  wave_affine_scan replaces each lane's pair by the composition
+// of the pairs of lanes 0 .. lane, in lane order (an inclusive scan over the
+// 64 lanes of a wave), in six steps of cross-lane moves: DPP shifts by 1, 2,
+// 4 and 8 lanes inside each row of 16, then the last lane of row 0 into row
+// 1 and of row 2 into row 3 (row_bcast:15), then lane 31 into rows 2 and 3
+// (row_bcast:31).  A lane whose source lies outside the row, or whose row is
+// masked off, takes the identity.  Every lane of the wave must be active.
+
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_or(float identity, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, identity),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROWMASK, 0xF, false));
+}
+
+// (a, b) <- (a_prev, b_prev) o (a, b) with the pair CTRL brings from another lane
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ void affine_step(float &a, float &b) {
+  const float ap = dpp_or<CTRL, ROWMASK>(1.0f, a);
+  const float bp = dpp_or<CTRL, ROWMASK>(0.0f, b);
+  b = fmaf(a, bp, b);
+  a = ap * a;
+}
+
+__device__ __forceinline__ void wave_affine_scan(float &a, float &b) {
+  affine_step<0x111, 0xF>(a, b);  // row_shr:1
+  affine_step<0x112, 0xF>(a, b);  // row_shr:2
+  affine_step<0x114, 0xF>(a, b);  // row_shr:4
+  affine_step<0x118, 0xF>(a, b);  // row_shr:8
+  affine_step<0x142, 0xA>(a, b);  // row_bcast:15 into rows 1 and 3
+  affine_step<0x143, 0xC>(a, b);  // row_bcast:31 into rows 2 and 3
+}
+
 // Returns z (always 0) through an opaque register move that reads every 32-bit
 // word of the given values: code whose operands depend on the result cannot be
 // scheduled before those values are computed and read.

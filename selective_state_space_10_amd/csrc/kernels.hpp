@@ -92,6 +92,17 @@ constexpr int64_t kNoAllocScratchBytes = (int64_t)16 << 20;
 // device; the array itself lives in scan_fwd.hip).
 hipError_t noalloc_scratch(void **ptr);
 
+// Scan of affine maps along rows: h[r, i] = a[r, i] h[r, i-1] + b[r, i] in scan
+// order (from the last element to the first if reverse), from h0[r] (0 if
+// null).  All (rows, len) fp32, row-major.
+struct AffineScanArgs {
+  int64_t rows, len;
+  const float *a, *b, *h0;
+  float *h;
+  int reverse;
+};
+hipError_t launch_affine_scan(const AffineScanArgs &a, hipStream_t stream);
+
 int64_t fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype);
 int64_t bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype);
 int64_t bwd_conv_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype);

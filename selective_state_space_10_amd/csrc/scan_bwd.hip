@@ -554,18 +554,32 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
 
 // Second phase of a sequence split: the adjoint entering every segment from
 // the right, carry[S-1] = dh_final, carry[s-1] = exp(A sum dt over s) carry[s]
-// + lamloc[s].
+// + lamloc[s]: a scan of the segments' affine maps from the last segment to
+// the first.  One wave per (b, d, n), segments on the lanes in that order (64
+// at a time), composed by the wave-wide associative scan.
 __global__ void __launch_bounds__(256) bwd_seg_combine_kernel(BwdArgs a, BwdWs ws) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b, d, n)
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, d, n): uniform over the wave
   if (i >= a.B * a.D * a.N) return;
   const int64_t n = i % a.N, d = (i / a.N) % a.D, b = i / (a.N * a.D);
   const int64_t S = ws.nseg;
   const float Ap = a.A[d * a.N + n] * kLog2e;
-  float c = a.dh_final ? a.dh_final[i] : 0.0f;
-  for (int64_t s = S - 1; s >= 0; --s) {
-    ws.carry[((b * S + s) * a.D + d) * a.N + n] = c;
-    if (s > 0)
-      c = fmaf(fast_exp2(Ap * ws.dsum[(b * S + s) * a.D + d]), c, ws.lamloc[((b * S + s) * a.D + d) * a.N + n]);
+  auto slot = [&](int64_t sg) { return ((b * S + sg) * a.D + d) * a.N + n; };
+  float carry = a.dh_final ? a.dh_final[i] : 0.0f;
+  if (lane == 0) ws.carry[slot(S - 1)] = carry;
+  for (int64_t k0 = 0; k0 + 1 < S; k0 += 64) {
+    const int64_t k = k0 + lane;
+    const bool valid = k + 1 < S;
+    const int64_t sg = S - 1 - k;  // the segment whose map this lane holds
+    float x = 1.0f, y = 0.0f;      // identity past the first segment
+    if (valid) {
+      x = fast_exp2(Ap * ws.dsum[(b * S + sg) * a.D + d]);
+      y = ws.lamloc[slot(sg)];
+    }
+    wave_affine_scan(x, y);
+    const float c = fmaf(x, carry, y);  // the adjoint leaving segment sg - 1 on the right
+    if (valid) ws.carry[slot(sg - 1)] = c;
+    carry = __shfl(c, 63, 64);
   }
 }
 
@@ -760,7 +774,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
                        a, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nst = a.B * a.D * a.N;
-    hipLaunchKernelGGL(bwd_seg_combine_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, a, ws);
+    hipLaunchKernelGGL(bwd_seg_combine_kernel, dim3((unsigned)((nst + 3) / 4)), dim3(256), 0, s, a, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (conv) {

@@ -763,19 +763,31 @@ static void launch_ws(const FwdArgs &a, dim3 grid, hipStream_t s) {
 }
 
 // Second phase of a sequence split: the state entering every segment,
-// h_in[0] = h0, h_in[s+1] = exp(A * sum of dt over s) * h_in[s] + h_loc[s]
-// (composition of the affine maps h -> a h + b of consecutive segments).
+// h_in[0] = h0, h_in[s+1] = exp(A * sum of dt over s) * h_in[s] + h_loc[s],
+// i.e. an exclusive scan of the segments' affine maps.  One wave per (b, d, n),
+// segments on the lanes (64 at a time), composed by the wave-wide associative
+// scan; the state is carried from one piece of 64 segments to the next.
 __global__ void __launch_bounds__(256) fwd_seg_combine_kernel(FwdArgs a, int64_t nseg) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b, d, n)
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, d, n): uniform over the wave
   if (i >= a.B * a.D * a.N) return;
   const int64_t n = i % a.N, d = (i / a.N) % a.D, b = i / (a.N * a.D);
   const float Ap = a.A[d * a.N + n] * kLog2e;
-  float h = a.h0 ? a.h0[i] : 0.0f;
-  for (int64_t s = 0; s < nseg; ++s) {
-    a.seg_state[((b * nseg + s) * a.D + d) * a.N + n] = h;
-    if (s + 1 < nseg)
-      h = fmaf(fast_exp2(Ap * a.seg_dsum[(b * nseg + s) * a.D + d]), h,
-               a.seg_hloc[((b * nseg + s) * a.D + d) * a.N + n]);
+  auto slot = [&](int64_t sg) { return ((b * nseg + sg) * a.D + d) * a.N + n; };
+  float carry = a.h0 ? a.h0[i] : 0.0f;
+  if (lane == 0) a.seg_state[slot(0)] = carry;
+  for (int64_t s0 = 0; s0 + 1 < nseg; s0 += 64) {
+    const int64_t sg = s0 + lane;  // the segment whose map this lane holds
+    const bool valid = sg + 1 < nseg;
+    float x = 1.0f, y = 0.0f;      // identity past the last map
+    if (valid) {
+      x = fast_exp2(Ap * a.seg_dsum[(b * nseg + sg) * a.D + d]);
+      y = a.seg_hloc[slot(sg)];
+    }
+    wave_affine_scan(x, y);
+    const float h = fmaf(x, carry, y);  // the state entering segment sg + 1
+    if (valid) a.seg_state[slot(sg + 1)] = h;
+    carry = __shfl(h, 63, 64);
   }
 }
 
@@ -874,7 +886,7 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nst = a.B * a.D * a.N;
-  hipLaunchKernelGGL(fwd_seg_combine_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, a, nseg);
+  hipLaunchKernelGGL(fwd_seg_combine_kernel, dim3((unsigned)((nst + 3) / 4)), dim3(256), 0, s, a, nseg);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (kWs) {  // the segments' full scans

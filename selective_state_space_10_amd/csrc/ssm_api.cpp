@@ -135,6 +135,25 @@ int ssm_scan_fwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate
   return SSM_OK;
 }
 
+int ssm_affine_scan(int64_t rows, int64_t len, const float *a, const float *b, const float *h0,
+                    float *h, int reverse, void *hip_stream) {
+  g_last_error[0] = 0;
+  if (rows < 1 || len < 1)
+    return fail(SSM_ERR_BAD_SHAPE, "rows=%lld and len=%lld must be >= 1", (long long)rows, (long long)len);
+  int64_t n;
+  if (!mul_ok(rows, len, &n)) return fail(SSM_ERR_BAD_SHAPE, "rows * len overflows 64-bit offsets");
+  if (rows > 4 * (int64_t)0x7fffffff)  // four rows per workgroup, workgroups are a grid dimension
+    return fail(SSM_ERR_UNSUPPORTED, "rows=%lld exceeds 4 * (2^31 - 1)", (long long)rows);
+  if (reverse != 0 && reverse != 1) return fail(SSM_ERR_UNSUPPORTED, "reverse=%d is neither 0 nor 1", reverse);
+  const Ptr ps[] = {{"a", a, true}, {"b", b, true}, {"h", h, true}, {"h0", h0, false}};
+  for (const Ptr &q : ps) {
+    if (q.required && q.p == nullptr) return fail(SSM_ERR_NULL_ARG, "%s is NULL", q.name);
+    if (((uintptr_t)q.p & 3u) != 0) return fail(SSM_ERR_ALIGNMENT, "%s is not 4-byte aligned", q.name);
+  }
+  ssm::AffineScanArgs args{rows, len, a, b, h0, h, reverse};
+  return hip_status(ssm::launch_affine_scan(args, (hipStream_t)hip_stream), "ssm_affine_scan launch");
+}
+
 int ssm_scan_fwd_ex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
                     const void *u, const void *delta, const float *A, const void *Bmat,
                     const void *Cmat, const float *Dskip, const void *z, const float *delta_bias,

@@ -286,6 +286,28 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delt
     return y
 
 
+def affine_scan(a, b, h0=None, reverse=False):
+    """Scan of affine maps along the last axis: h[..., i] = a[..., i] h[..., i-1]
+    + b[..., i] in scan order (last to first if ``reverse``), starting from h0
+    (shape a.shape[:-1], zeros if None).  a, b fp32 on one GPU, same shape."""
+    if not isinstance(a, torch.Tensor) or a.dim() < 1:
+        raise ValueError("a must be a tensor with at least one dimension")
+    dev = a.device
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {dev}")
+    _need("a", a, tuple(a.shape), torch.float32, dev)
+    _need("b", b, tuple(a.shape), torch.float32, dev)
+    _need("h0", h0, tuple(a.shape[:-1]), torch.float32, dev, optional=True)
+    length = a.shape[-1]
+    rows = a.numel() // max(length, 1)
+    h = torch.empty_like(a)
+    with torch.cuda.device(dev):
+        st = _lib.load().ssm_affine_scan(rows, length, _ptr(a), _ptr(b), _ptr(h0), _ptr(h),
+                                         int(bool(reverse)), _stream(dev))
+    _lib.check(st)
+    return h
+
+
 class SelectiveScanFn(torch.autograd.Function):
     """Autograd wrapper: forward saves the chunk-boundary states, backward
     recomputes the states inside each chunk from them."""

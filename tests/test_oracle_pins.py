@@ -279,3 +279,47 @@ def test_p10_softplus_silu(oracle_lib):
         assert oracle_lib.softplus(x) == pytest.approx(float(np.logaddexp(0.0, x)), rel=1e-15,
                                                        abs=1e-300)
         assert oracle_lib.silu(x) == pytest.approx(x * float(expit(x)), rel=1e-15, abs=1e-300)
+
+
+# --------------------------------------------------------------------------
+# P-19 the scan of affine maps (the fold the library's wave-wide scan and the
+# segment composition compute): exact against a fold in rational arithmetic,
+# equal to the recurrence's own state trajectory, and reversal.
+# --------------------------------------------------------------------------
+def test_p19_affine_scan_exact_rational_fold(oracle_lib):
+    """a = k/8, b, h0 small integers: every value is exact in fp64, so the fp64
+    fold must equal the fold in fractions.Fraction digit for digit."""
+    rng = np.random.default_rng(19)
+    rows, length = 3, 14
+    a = rng.integers(-8, 9, size=(rows, length)) / 8.0
+    b = rng.integers(-10, 11, size=(rows, length)).astype(np.float64)
+    h0 = rng.integers(-5, 6, size=rows).astype(np.float64)
+    for reverse in (False, True):
+        got = oracle_lib.affine_scan(a, b, h0, reverse=reverse)
+        for r in range(rows):
+            s = Fraction(int(h0[r]))
+            order = range(length - 1, -1, -1) if reverse else range(length)
+            for i in order:
+                s = Fraction(int(a[r, i] * 8), 8) * s + Fraction(int(b[r, i]))
+                assert got[r, i] == float(s) and Fraction(got[r, i]) == s
+
+
+def test_p19_affine_scan_is_the_recurrence(oracle_lib):
+    """With a_t = exp(dt_t A) and b_t = dt_t B_t u_t (one channel, one state),
+    the fold is the scan's state trajectory, which the NumPy twin returns."""
+    p = rand_problem(1, 40, 1, 1, seed=29, with_h0=True, with_z=False, with_D=False)
+    _, _, _, states = oracle_np.scan_fwd(**p, return_states=True)
+    dt = np.logaddexp(0.0, (p["delta"] + p["delta_bias"]).numpy()[0, :, 0])
+    a = np.exp(dt * p["A"].numpy()[0, 0])
+    b = dt * p["B"].numpy()[0, :, 0] * p["u"].numpy()[0, :, 0]
+    h = oracle_lib.affine_scan(a[None], b[None], p["h0"].numpy()[0, 0][None])
+    assert nmax_err(h[0], states[0, :, 0, 0]) < 1e-14
+
+
+def test_p19_affine_scan_reverse_is_flipped_forward(oracle_lib):
+    rng = np.random.default_rng(3)
+    a, b = rng.uniform(0.2, 1.0, (2, 30)), rng.standard_normal((2, 30))
+    h0 = rng.standard_normal(2)
+    rev = oracle_lib.affine_scan(a, b, h0, reverse=True)
+    fwd = oracle_lib.affine_scan(a[:, ::-1], b[:, ::-1], h0)
+    assert np.array_equal(rev, fwd[:, ::-1])

@@ -51,6 +51,49 @@ def test_p9_backward_matches_finite_differences(impl, opts):
         assert err < 2e-7, (name, err)
 
 
+@pytest.mark.parametrize("impl", [oracle_c, oracle_np], ids=["c", "np"])
+@pytest.mark.parametrize("opts", [dict(), dict(zoh=True), dict(reverse=True)],
+                         ids=["plain", "zoh", "reverse"])
+def test_p9_dot_product_linear_part(impl, opts):
+    """Without the gate, and with delta, B, C fixed, (y, h_final) is linear in
+    (u, h0), so the backward's du, dh0 must be the exact adjoint of that map:
+    <J v, w> = <v, J^T w> for random v = (v_u, v_h0) and w = (w_y, w_h) to
+    rounding (the forward applied to v is J v itself)."""
+    kw = {k: v for k, v in opts.items()}
+    p = rand_problem(2, 19, 5, 4, seed=41, with_h0=True, with_z=False)
+    g = torch.Generator().manual_seed(8)
+    vu = torch.randn(p["u"].shape, generator=g, dtype=torch.float64)
+    vh = torch.randn(p["h0"].shape, generator=g, dtype=torch.float64)
+    wy = torch.randn(p["u"].shape, generator=g, dtype=torch.float64).numpy()
+    wh = torch.randn(p["h0"].shape, generator=g, dtype=torch.float64).numpy()
+    q = dict(p, u=vu, h0=vh, D=p["D"])
+    yv, hv, _ = impl.scan_fwd(**q, **kw)
+    lhs = float((yv * wy).sum() + (hv * wh).sum())
+    gr = impl.scan_bwd(**q, dy=wy, dh_final=wh, **kw)
+    rhs = float((gr["du"] * vu.numpy()).sum() + (gr["dh0"] * vh.numpy()).sum())
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs)), (lhs, rhs)
+
+
+@pytest.mark.parametrize("impl", [oracle_c, oracle_np], ids=["c", "np"])
+def test_p9_dot_product_full_map(impl):
+    """The whole nonlinear map, all nine inputs at once: the directional
+    derivative along a random direction v (central difference of the fp64
+    forward) equals <v, J^T w> from the backward."""
+    p = rand_problem(2, 9, 3, 2, seed=43, with_h0=True)
+    g = torch.Generator().manual_seed(9)
+    w = torch.randn(p["u"].shape, generator=g, dtype=torch.float64).numpy()
+    G = torch.randn(p["h0"].shape, generator=g, dtype=torch.float64).numpy()
+    names = [k for k in GRAD_OF if p.get(k) is not None]
+    v = {k: torch.randn(p[k].shape, generator=g, dtype=torch.float64) for k in names}
+    grads = impl.scan_bwd(**p, dy=w, dh_final=G)
+    rhs = sum(float((grads[GRAD_OF[k]] * v[k].numpy()).sum()) for k in names)
+    eps = 1e-6
+    plus = dict(p, **{k: p[k] + eps * v[k] for k in names})
+    minus = dict(p, **{k: p[k] - eps * v[k] for k in names})
+    lhs = (_loss(impl, plus, w, G) - _loss(impl, minus, w, G)) / (2 * eps)
+    assert abs(lhs - rhs) <= 1e-7 * max(1.0, abs(rhs)), (lhs, rhs)
+
+
 def test_p9_backward_without_final_cotangent():
     p = rand_problem(1, 5, 2, 3, seed=2)
     w = np.random.default_rng(0).normal(size=(1, 5, 2))

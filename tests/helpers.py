@@ -35,3 +35,22 @@ def rand_problem(B, L, D, N, seed=0, *, with_z=True, with_D=True, with_bias=True
     if dtype != torch.float64:
         p = {k: (v.to(dtype) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
     return p
+
+
+def parity_report(name, got, ref) -> dict:
+    """The per-output-tensor error reported beside the gated metric: the
+    normalised max error, the largest per-element relative error over entries
+    with |ref| >= 1e-3 max|ref|, its index, and the NaN count (which must be 0).
+    Printed, so that it appears in the test log."""
+    g = np.asarray(got.detach().cpu().double() if hasattr(got, "detach") else got, np.float64)
+    r = np.asarray(ref.detach().cpu().double() if hasattr(ref, "detach") else ref, np.float64)
+    nan = int(np.isnan(g).sum())
+    scale = float(np.abs(r).max()) if r.size else 0.0
+    mask = np.abs(r) >= 1e-3 * scale
+    rel = np.where(mask, np.abs(g - r) / np.where(mask, np.abs(r), 1.0), 0.0)
+    worst = np.unravel_index(int(np.argmax(rel)), rel.shape) if rel.size else ()
+    rep = {"tensor": name, "nmax_err": nmax_err(g, r) if not nan else float("nan"),
+           "max_rel_err_significant": float(rel.max()) if rel.size else 0.0,
+           "worst_index": tuple(int(i) for i in worst), "nan_count": nan}
+    print("parity", rep, flush=True)
+    return rep

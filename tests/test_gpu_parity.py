@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from oracle import oracle_c
-from tests.helpers import nmax_err
+from tests.helpers import nmax_err, parity_report
 from workloads import WORKLOADS, cotangent, decode_inputs, scan_inputs, workload_inputs
 
 pytestmark = pytest.mark.gpu
@@ -171,8 +171,9 @@ def _sampled_fwd(ssm, idx, nsample, seed_dev="cuda"):
     ps = _slice_channels(p, sel.to(p["u"].device))
     yo, hfo, cso = oracle_c.scan_fwd(**_oracle_kwargs(ps), chunk_len=T if want_cs else None)
     tol = TOL[w.io_dtype]
-    assert nmax_err(y[:, :, sel.cuda()], yo) <= tol
-    assert nmax_err(hf[:, sel.cuda()], hfo) <= tol
+    for name, got, ref in (("y", y[:, :, sel.cuda()], yo), ("h_final", hf[:, sel.cuda()], hfo)):
+        rep = parity_report(f"{w.name}:{name}", got, ref)
+        assert rep["nan_count"] == 0 and rep["nmax_err"] <= tol
     if want_cs:
         assert nmax_err(cs[:, :, :, sel.cuda()].permute(0, 1, 3, 2), cso) <= tol
     return p, y
@@ -411,11 +412,11 @@ def test_bwd_workload4_full_size(ssm):
     tol = TOL[w.io_dtype]
     sc = sel.cuda()
     for k in ("du", "ddelta", "dz"):
-        assert nmax_err(gr[k][:, :, sc], go[k]) <= tol, k
+        assert parity_report(f"million-length:{k}", gr[k][:, :, sc], go[k])["nmax_err"] <= tol, k
         assert int(torch.count_nonzero(gr[k][:, :, ~mask.cuda()])) == 0, k
     for k in ("dB", "dC"):
-        assert nmax_err(gr[k], go[k]) <= tol, k
-    assert nmax_err(gr["dA"][sc], go["dA"]) <= tol
+        assert parity_report(f"million-length:{k}", gr[k], go[k])["nmax_err"] <= tol, k
+    assert parity_report("million-length:dA", gr["dA"][sc], go["dA"])["nmax_err"] <= tol
     for k in ("dD", "ddelta_bias"):
         assert nmax_err(gr[k][sc], go[k]) <= tol, k
 

@@ -16,7 +16,9 @@ namespace {
 
 constexpr int kChains = 8;     // independent dependency chains per lane
 constexpr int kGroups = 8;     // unrolled groups per loop iteration
-constexpr int kLdsBytes = 96 * 1024;  // more than half of a CU's LDS: one workgroup per CU
+// Dynamic LDS requested at launch (never touched): more than half of a CU's
+// LDS, so only one workgroup fits on a CU.
+constexpr int kLdsBytes = 96 * 1024;
 
 // KIND 0: v_fma_f32 only.  KIND 1: v_exp_f32 only.  KIND 2: one v_exp_f32
 // then four v_fma_f32, each on its own chain (the recurrence's 1:4 mix, no
@@ -26,7 +28,6 @@ constexpr int kLdsBytes = 96 * 1024;  // more than half of a CU's LDS: one workg
 // into one of two running sums.
 template <int KIND>
 __global__ void probe_kernel(int64_t iters, float *out) {
-  extern __shared__ float lds[];  // requested, never used: caps workgroups per CU at one
   float x[kChains], e[kChains];
   const float a = 0.999f + 1e-7f * (float)(threadIdx.x & 7), b = 1e-3f;
 #pragma unroll
@@ -73,7 +74,6 @@ __global__ void probe_kernel(int64_t iters, float *out) {
   float s = y0 + y1;
 #pragma unroll
   for (int c = 0; c < kChains; ++c) s += x[c] + e[c];
-  if (s == 12345.678f) lds[threadIdx.x] = s;  // never true; keeps the LDS request
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
@@ -81,13 +81,11 @@ __global__ void probe_kernel(int64_t iters, float *out) {
 // SIMD_ID field, bits 5:4, of the HW_ID hardware register), for a workgroup of
 // `threads` threads that requests `lds` bytes of LDS.  One value per wave.
 __global__ void placement_kernel(int *out) {
-  extern __shared__ float lds[];
   const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 4);  // hwreg(HW_REG_HW_ID)
   const int wave = threadIdx.x >> 6;
   const int waves = (blockDim.x + 63) >> 6;
   if ((threadIdx.x & 63) == 0) {
     out[(int64_t)blockIdx.x * waves + wave] = (int)((hw >> 4) & 3) | (int)(((hw >> 8) & 15) << 4);
-    if (hw == 0xffffffffu) lds[0] = 1.0f;  // never true; keeps the LDS request
   }
 }
 

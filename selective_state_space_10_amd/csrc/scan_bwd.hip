@@ -391,9 +391,9 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
       const int64_t t = t0 + tl;
       float ddl = 0.0f;
       if (t < te && dv) {
-        float pre = 0.0f, dua = 0.0f, dda = 0.0f;
+        float pre = Q[0][tq][0][lane], dua = Q[1][tq][0][lane], dda = Q[2][tq][0][lane];
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
+        for (int ww = 1; ww < NW; ++ww) {
           pre += Q[0][tq][ww][lane];
           dua += Q[1][tq][ww][lane];
           dda += Q[2][tq][ww][lane];

@@ -12,6 +12,7 @@ line (rank 0).
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 ``--workload`` also accepts the other shapes and options (mamba-2.8b-layer-fwd,
+the 32K-context forward at the 2.8b width (mamba-2.8b-32k-fwd),
 decode-state-update, million-length-fwd, million-length-bwd,
 mamba-370m-layer-bwd, the 370m forward with the exact zero-order hold, with one
 step size per token, bidirectional or with the fused convolution, the 370m
@@ -44,7 +45,8 @@ WORKLOAD_NAMES = ["mamba-370m-layer-fwd", "mamba-2.8b-layer-fwd", "decode-state-
                   "million-length-fwd", "million-length-bwd", "mamba-370m-layer-bwd",
                   "mamba-370m-layer-fwd-zoh", "mamba-370m-layer-fwd-token-delta",
                   "mamba-370m-layer-bidirectional", "decode-state-update-zoh",
-                  "mamba-370m-layer-fwd-conv4", "mamba-370m-layer-bwd-conv4", "mamba-370m-layer-bwd-zoh"]
+                  "mamba-370m-layer-fwd-conv4", "mamba-370m-layer-bwd-conv4", "mamba-370m-layer-bwd-zoh",
+                  "mamba-2.8b-32k-fwd"]
 METRIC = "selective-scan fwd tokens·channels/s and HBM GB/s (% of peak), Mamba-370m shape"
 # The only throughput figure the source pages give for the method is relative and
 # names no hardware, precision or workload: context beside the kernel's rate, not
@@ -711,6 +713,8 @@ def main():
     elif wl == "million-length-fwd":
         args.rotate = 1
         line = bench_fwd(args, 4, wl)
+    elif wl == "mamba-2.8b-32k-fwd":
+        line = bench_fwd(args, 5, wl)
     elif wl == "decode-state-update":
         line = bench_decode(args)
     elif wl == "decode-state-update-zoh":

@@ -75,14 +75,15 @@ inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 // Sequence split: when batch rows x channel tiles cannot fill the GPU, cut the
 // sequence into segments (multiples of 256 steps, at least kMinSeg long)
-// aiming at kTarget workgroups.  Depends on sizes only.
+// filling at most kTarget workgroups, two whole rounds of one workgroup per CU
+// on an MI355X (256 CUs).  Depends on sizes only.
 constexpr int64_t kMinSeg = 2048;
 constexpr int64_t kTarget = 512;
 
 int64_t bwd_split_len(int64_t B, int64_t L, int64_t D) {
   const int64_t tiles = B * ((D + kCPW - 1) / kCPW);
   if (tiles >= 192 || L < 2 * kMinSeg) return 0;
-  int64_t nseg = (kTarget + tiles - 1) / tiles;
+  int64_t nseg = kTarget / tiles;  // whole rounds: a partly filled round costs a full one
   if (nseg > L / kMinSeg) nseg = L / kMinSeg;
   if (nseg < 2) return 0;
   int64_t len = (L + nseg - 1) / nseg;

@@ -792,21 +792,26 @@ __global__ void __launch_bounds__(256) fwd_seg_combine_kernel(FwdArgs a, int64_t
 }
 
 // Sequence split for problems with too few channel tiles to fill the GPU:
-// segments of at least kMinSeg steps, aiming at kSplitTarget workgroups of 32
-// channels.  Depends on sizes only, so the workspace query agrees with it.
+// segments of at least kMinSeg steps.  With 16 states both passes run the
+// wave-specialised kernel on 64-channel tiles, one workgroup per CU, so the
+// segments fill one round of kSplitCUs (the CUs of an MI355X): a second,
+// partly filled round would cost as much as the first.  Other state counts
+// aim at kSplitTarget workgroups of 32 channels.  Depends on sizes only, so
+// the workspace query agrees with it.
 constexpr int64_t kMinSeg = 4096;
 constexpr int64_t kSplitTarget = 512;
+constexpr int64_t kSplitCUs = 256;
 
 // The wave-specialised kernel addresses a segment with 32-bit byte offsets:
 // (segment length + 64) rows of a (B,L,D) array must stay below 2^31 bytes.
 static int64_t ws_max_rows(int64_t D, int64_t io_bytes) { return ((int64_t)1 << 31) / (D * io_bytes) - 64; }
 
 // Segment length of a sequence split (0: no split), io_bytes per element.
-static int64_t split_len(int64_t B, int64_t L, int64_t D, int64_t io_bytes) {
+static int64_t split_len(int64_t B, int64_t L, int64_t D, int64_t N, int64_t io_bytes) {
   const int64_t tiles64 = B * ((D + 63) / 64);
   if (tiles64 >= 128 || L < 2 * kMinSeg) return 0;
   const int64_t tiles32 = B * ((D + 31) / 32);
-  int64_t nseg = (kSplitTarget + tiles32 - 1) / tiles32;
+  int64_t nseg = N == 16 ? kSplitCUs / tiles64 : (kSplitTarget + tiles32 - 1) / tiles32;
   if (nseg > L / kMinSeg) nseg = L / kMinSeg;
   if (nseg < 2) return 0;
   int64_t len = (L + nseg - 1) / nseg;
@@ -845,7 +850,7 @@ static int pick_cpw(const FwdArgs &a) {
   constexpr int mincpw = 64 * NPL / N > 16 ? 64 * NPL / N : 16;
   if (env == 16 || env == 32 || env == 64 || (N == 16 && env == 80)) return env < mincpw ? mincpw : env;
   if (mincpw > 32) return 64;
-  if (split_len(a.B, a.L, a.D, 4)) return 32;  // split sequences use 32-channel tiles (the io size only caps the length)
+  if (split_len(a.B, a.L, a.D, a.N, 4)) return 32;  // split sequences use 32-channel tiles (the io size only caps the length)
   const int64_t wg64 = a.B * ((a.D + 63) / 64);
   if (wg64 <= device_cus()) return 64;
   // 80-channel tiles (16 states only) where they fit in one round over the
@@ -863,7 +868,7 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   constexpr int IPT = T * (CPW / 4) / (64 * NW);
   constexpr int PD = IPT <= 2 ? 2 : 1;
   FwdArgs a = a0;
-  a.seg_len = split_len(a.B, a.L, a.D, sizeof(IO));
+  a.seg_len = split_len(a.B, a.L, a.D, a.N, sizeof(IO));
   const unsigned tiles = (unsigned)((a.D + CPW - 1) / CPW);
   if (a.seg_len == 0) {
     hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 0, ZOH, FLAGS>), dim3(tiles, (unsigned)a.B, 1), dim3(64 * NW), 0, s,
@@ -908,7 +913,7 @@ static FwdPlan plan_fwd_t(const FwdArgs &a, int64_t io_bytes) {
   // options use one tile width (fewer instantiations); the plain scan picks its own
   constexpr int OCPW = mincpw > 32 ? 64 : 32;
   FwdPlan pl{};
-  pl.segment_len = split_len(a.B, a.L, a.D, io_bytes);
+  pl.segment_len = split_len(a.B, a.L, a.D, a.N, io_bytes);
   pl.segments = pl.segment_len ? (a.L + pl.segment_len - 1) / pl.segment_len : 1;
   if (N == 16 && pl.segment_len == 0 && a.L <= ws_max_rows(a.D, io_bytes)) {
     // 16 states, no sequence split, and every row of a (B,L,D) array within
@@ -1025,7 +1030,7 @@ hipError_t noalloc_scratch(void **ptr) {
 }
 
 int64_t fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype) {
-  const int64_t len = split_len(B, L, D, io_dtype == 0 ? 4 : 2);
+  const int64_t len = split_len(B, L, D, N, io_dtype == 0 ? 4 : 2);
   if (len == 0) return 0;
   const int64_t nseg = (L + len - 1) / len;
   return (2 * B * nseg * D * N + B * nseg * D) * 4;

@@ -201,6 +201,7 @@ ZOH, REV, TOK, ACC = 1, 2, 4, 8
     ((8, 40, 3336, 16), 0, REV | TOK, 0, (1, 32, 1)),
     ((1, 37, 20480, 16), 0, 0, 0, (1, 80, 1)),
     ((1, 1 << 20, 1024, 16), 1, 0, 0, (1, 64, 16)),    # million-length: split into 16 segments
+    ((1, 32768, 5120, 16), 1, 0, 0, (1, 64, 3)),       # 32K context: 3 x 80 tiles fill one round
     ((1, 65536, 8192, 16), 0, 0, 0, (0, 64, 1)),       # a row spans 2 GiB: 64-bit offsets
     ((2, 300, 72, 8), 0, 0, 0, (0, 64, 1)),
     ((3, 97, 136, 8), 0, ZOH, 0, (0, 32, 1)),

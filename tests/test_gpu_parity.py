@@ -191,6 +191,16 @@ def test_fwd_workload4_full_size(ssm):
     _sampled_fwd(ssm, 4, 4)
 
 
+def test_fwd_32k_context_full_size(ssm):
+    """Batch 1, length 32768 (the context length the pages state), 5120
+    channels, bf16: too few channel tiles for the GPU, so the launcher splits
+    the sequence; sampled channels against the oracle."""
+    w = WORKLOADS[5]
+    plan = ssm.scan_fwd_plan(w.batch, w.seqlen, w.dim, w.dstate, w.io_dtype)
+    assert plan["segments"] > 1, plan
+    _sampled_fwd(ssm, 5, 8)
+
+
 @pytest.mark.parametrize("reverse", [False, True], ids=["forward", "reverse"])
 @pytest.mark.parametrize("L", [65472, 65536])
 def test_fwd_rows_near_2gib(ssm, L, reverse):

@@ -58,6 +58,8 @@ WORKLOADS = {
                 outputs=("y", "state")),
     4: Workload("million-length-fwd-bwd", 1, 1 << 20, 1024, 16, torch.bfloat16, "fwd+bwd",
                 outputs=("y", "chunk_states", "du", "ddelta", "dA", "dB", "dC", "dD", "dz")),
+    # the one scan length the pages state (a 32K context), at the Mamba-2.8b width
+    5: Workload("mamba-2.8b-32k-fwd", 1, 32768, 5120, 16, torch.bfloat16, "fwd", outputs=("y",)),
 }
 
 

@@ -826,8 +826,8 @@ static int64_t split_len(int64_t B, int64_t L, int64_t D, int64_t N, int64_t io_
 // (84 KB of LDS), an 80-channel one too (104 KB); 32-channel tiles fit two
 // (16 states) or three (fwd_kernel) per CU.  Measured on MI355X: 64-channel
 // tiles are fastest while the grid fits in one round over the CUs; beyond
-// that, 80-channel tiles (16 states) if they fit in one round, else 32-channel
-// tiles, avoid a mostly idle second round.  SSM_FWD_CPW overrides the choice
+// that, 16 states take the width with the fewest costed rounds (pick_cpw),
+// other state counts take 32-channel tiles.  SSM_FWD_CPW overrides the choice
 // (tuning only).
 static int device_cus() {
   static int cus = [] {
@@ -851,12 +851,27 @@ static int pick_cpw(const FwdArgs &a) {
   if (env == 16 || env == 32 || env == 64 || (N == 16 && env == 80)) return env < mincpw ? mincpw : env;
   if (mincpw > 32) return 64;
   if (split_len(a.B, a.L, a.D, a.N, 4)) return 32;  // split sequences use 32-channel tiles (the io size only caps the length)
+  const int64_t cus = device_cus();
   const int64_t wg64 = a.B * ((a.D + 63) / 64);
-  if (wg64 <= device_cus()) return 64;
-  // 80-channel tiles (16 states only) where they fit in one round over the
-  // CUs and 64-channel tiles do not: one workgroup per CU does 1.25 times the
-  // work, instead of a second round for the tiles left over
-  if (N == 16 && a.B * ((a.D + 79) / 80) <= device_cus()) return 80;
+  if (wg64 <= cus) return 64;
+  if constexpr (N == 16) {
+    // More tiles than one round of 64 channels: the width with the lowest
+    // cost in rounds.  A partly filled round costs as much as a full one.  A
+    // round of 64- or 80-channel tiles (one workgroup per CU) costs its width;
+    // a CU holding two 32-channel workgroups costs 83 and one alone 35
+    // (measured on MI355X: 16 x 2048 x 2048 fp32 takes 331 us on 64-channel
+    // tiles, 372 on 80, 400 on 32; 12 x 2048 x 2048 takes 285 on 32, 289 on
+    // 64; 8 x 4096 x 5120 bf16 takes 710 on 80, 795 on 64, 905 on 32).  The
+    // fused convolution has no 80-channel variant.
+    auto rounds = [&](int64_t wg) { return (wg + cus - 1) / cus; };
+    const int64_t wg32 = a.B * ((a.D + 31) / 32);
+    const int64_t full = wg32 / (2 * cus), rest = wg32 % (2 * cus);
+    const int64_t c32 = full * 83 + (rest == 0 ? 0 : rest > cus ? 83 : 35);
+    const int64_t c64 = rounds(wg64) * 64;
+    const int64_t c80 = a.conv_k ? INT64_MAX : rounds(a.B * ((a.D + 79) / 80)) * 80;
+    if (c64 <= c80 && c64 <= c32) return 64;
+    return c80 <= c32 ? 80 : 32;
+  }
   return 32;
 }
 

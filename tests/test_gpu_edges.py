@@ -77,11 +77,13 @@ def _assert_plan(ssm, p, tile, zoh=False, reverse=False, conv=0):
                          ids=["plain", "zoh", "reverse-per-token"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_many_channel_tiles(ssm, dtype, opts):
-    """More tiles than compute units even at 80 channels (8 rows x 42 tiles of
-    80 > 256): the 16-state forward takes 32-channel tiles (8 x 105, the last
-    one ragged: 8 of 32 channels), two workgroups per compute unit."""
+    """More tiles than one round over the compute units: 12 rows x 32 tiles of
+    64 or 12 x 26 of 80 need two rounds, while 12 x 64 tiles of 32 take one
+    round of two workgroups per compute unit and half a round of one, so the
+    16-state forward takes 32-channel tiles (the last one ragged: 24 of 32
+    channels)."""
     from tests.test_gpu_options import _check_fwd as _check_fwd_opts, _with_opts
-    p = _with_opts(_problem(8, 40, 3336, 16, dtype, seed=41, h0=True), opts.get("tok", False))
+    p = _with_opts(_problem(12, 40, 2040, 16, dtype, seed=41, h0=True), opts.get("tok", False))
     _assert_plan(ssm, p, 32, opts.get("zoh", False), opts.get("reverse", False))
     _check_fwd_opts(ssm, p, TOL[dtype], opts.get("zoh", False), opts.get("reverse", False))
 
@@ -89,11 +91,11 @@ def test_many_channel_tiles(ssm, dtype, opts):
 @pytest.mark.parametrize("opts", [dict(), dict(zoh=True, tok=True)], ids=["plain", "zoh-per-token"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_many_channel_tiles_fused_conv(ssm, dtype, opts):
-    """The fused convolution on 32-channel tiles (8 x 105 tiles), against the
+    """The fused convolution on 32-channel tiles (12 x 64 tiles), against the
     oracle's convolution followed by its scan."""
     from tests.test_gpu_conv import _conv_problem, _gpu_fwd as _conv_fwd, _okw
     zoh = opts.get("zoh", False)
-    p = _conv_problem(8, 40, 3336, 16, dtype, 4, seed=47, tok=opts.get("tok", False))
+    p = _conv_problem(12, 40, 2040, 16, dtype, 4, seed=47, tok=opts.get("tok", False))
     _assert_plan(ssm, p, 32, zoh=zoh, conv=4)
     T = ssm.chunk_len()
     y, hf, cs = _conv_fwd(ssm, _to(p, "cuda"), zoh, return_final_state=True, save_chunk_states=True)
@@ -115,6 +117,17 @@ def test_eighty_channel_tiles(ssm, dtype, opts):
     p = _with_opts(_problem(1, 37, 20480, 16, dtype, seed=43, h0=True), opts.get("tok", False))
     _assert_plan(ssm, p, 80, opts.get("zoh", False), opts.get("reverse", False))
     _check_fwd_opts(ssm, p, TOL[dtype], opts.get("zoh", False), opts.get("reverse", False))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_two_full_rounds_of_64_channel_tiles(ssm, dtype):
+    """16 rows x 32 tiles of 64 channels: exactly two rounds over 256 compute
+    units, which the forward prefers to 32-channel tiles (two rounds of two
+    workgroups per compute unit) and to 80-channel tiles (two rounds, 416
+    tiles)."""
+    p = _problem(16, 24, 2048, 16, dtype, seed=45, h0=True)
+    _assert_plan(ssm, p, 64)
+    _check_fwd(ssm, p, TOL[dtype])
 
 
 @pytest.mark.parametrize("z,Dskip", [(True, True), (False, False)], ids=["gated", "no-gate-no-skip"])

@@ -73,20 +73,39 @@ constexpr int64_t kConvRows = 64;  // rows per block of the convolution backward
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
-// Sequence split: when batch rows x channel tiles cannot fill the GPU, cut the
-// sequence into segments (multiples of 256 steps, at least kMinSeg long)
-// filling at most kTarget workgroups, two whole rounds of one workgroup per CU
-// on an MI355X (256 CUs).  Depends on sizes only.
+// Sequence split.  Workgroups (one per CU) run in rounds over the MI355X's
+// kCUs compute units, and a partly filled round costs as much as a full one.
+// A split into S segments costs R(S x tiles) / S rounds of the full backward
+// plus kMode1 of that for the first pass over S - 1 segments (the local
+// adjoint carries; measured at 0.23 of a full step), R(w) = ceil(w / kCUs).
+// Among the segment counts (1: no split) within 1% of the lowest cost, the
+// smallest that gives at least two rounds is taken (later workgroups fill in
+// behind the first round's slowest ones: 22.1 ms against 23.5 ms for 32
+// against 16 segments at the million-length shape), else the smallest.
+// Segments are multiples of 256 steps, at least kMinSeg long.  Depends on
+// sizes only.
 constexpr int64_t kMinSeg = 2048;
-constexpr int64_t kTarget = 512;
+constexpr int64_t kCUs = 256;
+constexpr double kMode1 = 0.23;
 
 int64_t bwd_split_len(int64_t B, int64_t L, int64_t D) {
   const int64_t tiles = B * ((D + kCPW - 1) / kCPW);
-  if (tiles >= 192 || L < 2 * kMinSeg) return 0;
-  int64_t nseg = kTarget / tiles;  // whole rounds: a partly filled round costs a full one
-  if (nseg > L / kMinSeg) nseg = L / kMinSeg;
-  if (nseg < 2) return 0;
-  int64_t len = (L + nseg - 1) / nseg;
+  const int64_t smax = L / kMinSeg < 1024 ? L / kMinSeg : 1024;
+  auto cost = [&](int64_t S) {
+    auto rounds = [](int64_t w) { return (double)((w + kCUs - 1) / kCUs); };
+    return (rounds(S * tiles) + (S > 1 ? kMode1 * rounds((S - 1) * tiles) : 0.0)) / (double)S;
+  };
+  double best = cost(1);
+  for (int64_t S = 2; S <= smax; ++S) best = cost(S) < best ? cost(S) : best;
+  int64_t pick = 0, first = 0;
+  for (int64_t S = 1; S <= (smax > 1 ? smax : 1); ++S) {
+    if (cost(S) > best * 1.01) continue;
+    if (!first) first = S;
+    if (S * tiles >= 2 * kCUs) { pick = S; break; }
+  }
+  if (!pick) pick = first;
+  if (pick < 2) return 0;
+  int64_t len = (L + pick - 1) / pick;
   len = (len + 255) / 256 * 256;
   return len;
 }

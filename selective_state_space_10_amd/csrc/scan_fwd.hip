@@ -793,14 +793,21 @@ __global__ void __launch_bounds__(256) fwd_seg_combine_kernel(FwdArgs a, int64_t
 
 // Sequence split for problems with too few channel tiles to fill the GPU:
 // segments of at least kMinSeg steps.  With 16 states both passes run the
-// wave-specialised kernel on 64-channel tiles, one workgroup per CU, so the
-// segments fill one round of kSplitCUs (the CUs of an MI355X): a second,
-// partly filled round would cost as much as the first.  Other state counts
-// aim at kSplitTarget workgroups of 32 channels.  Depends on sizes only, so
-// the workspace query agrees with it.
+// wave-specialised kernel on 64-channel tiles, one workgroup per CU, in rounds
+// over kSplitCUs (the CUs of an MI355X); a partly filled round costs as much as
+// a full one.  S segments cost R(S x tiles) / S rounds of the full pass plus
+// kSplitMode1 of that for the first pass over S - 1 segments (measured: 0.78
+// of a full step), R(w) = ceil(w / kSplitCUs).  Among the counts within 1% of
+// the lowest cost the smallest giving at least kSplitMinRounds rounds is taken
+// (later workgroups fill in behind earlier ones: at the million-length shape
+// 7.9 ms with one round of 16 segments, 7.3 with two, 7.2 with four), else
+// the smallest.  Other state counts aim at kSplitTarget workgroups of 32
+// channels.  Depends on sizes only, so the workspace query agrees with it.
 constexpr int64_t kMinSeg = 4096;
 constexpr int64_t kSplitTarget = 512;
 constexpr int64_t kSplitCUs = 256;
+constexpr double kSplitMode1 = 0.78;
+constexpr int64_t kSplitMinRounds = 4;
 
 // The wave-specialised kernel addresses a segment with 32-bit byte offsets:
 // (segment length + 64) rows of a (B,L,D) array must stay below 2^31 bytes.
@@ -811,7 +818,26 @@ static int64_t split_len(int64_t B, int64_t L, int64_t D, int64_t N, int64_t io_
   const int64_t tiles64 = B * ((D + 63) / 64);
   if (tiles64 >= 128 || L < 2 * kMinSeg) return 0;
   const int64_t tiles32 = B * ((D + 31) / 32);
-  int64_t nseg = N == 16 ? kSplitCUs / tiles64 : (kSplitTarget + tiles32 - 1) / tiles32;
+  int64_t nseg = (kSplitTarget + tiles32 - 1) / tiles32;
+  if (N == 16) {
+    const int64_t smax = L / kMinSeg < 1024 ? L / kMinSeg : 1024;
+    auto cost = [&](int64_t S) {
+      auto rounds = [](int64_t w) { return (double)((w + kSplitCUs - 1) / kSplitCUs); };
+      return (rounds(S * tiles64) + (S > 1 ? kSplitMode1 * rounds((S - 1) * tiles64) : 0.0)) / (double)S;
+    };
+    double best = cost(1);
+    for (int64_t S = 2; S <= smax; ++S) best = cost(S) < best ? cost(S) : best;
+    int64_t pick = 0, first = 0;
+    for (int64_t S = 1; S <= (smax > 1 ? smax : 1); ++S) {
+      if (cost(S) > best * 1.01) continue;
+      if (!first) first = S;
+      if (S * tiles64 >= kSplitMinRounds * kSplitCUs) {
+        pick = S;
+        break;
+      }
+    }
+    nseg = pick ? pick : first;
+  }
   if (nseg > L / kMinSeg) nseg = L / kMinSeg;
   if (nseg < 2) return 0;
   int64_t len = (L + nseg - 1) / nseg;

@@ -86,8 +86,8 @@ def test_version_and_queries(lib):
     assert lib.ssm_status_string(99) == b"unknown status"
 
 
-@pytest.mark.parametrize("L,D,io,nseg_uncapped", [(1 << 20, 1024, 0, 16), (1 << 22, 4096, 0, 4),
-                                                  (1 << 22, 4096, 1, 4)])
+@pytest.mark.parametrize("L,D,io,nseg_uncapped", [(1 << 20, 1024, 0, 64), (1 << 22, 4096, 0, 16),
+                                                  (1 << 22, 4096, 1, 16)])
 def test_fwd_split_segments_fit_32bit_offsets(lib, L, D, io, nseg_uncapped):
     """A split sequence's segments are what the forward workspace holds
     (per segment: two (D,N) state arrays and a D-vector of step-size sums). The
@@ -205,7 +205,7 @@ ZOH, REV, TOK, ACC = 1, 2, 4, 8
     ((8, 4096, 5120, 16), 1, 0, 4, (1, 64, 1)),        # ... no 80 with the convolution
     ((8, 40, 3336, 16), 0, 0, 0, (1, 64, 1)),          # 424 tiles of 64: two rounds beat 32
     ((1, 37, 20480, 16), 0, 0, 0, (1, 80, 1)),
-    ((1, 1 << 20, 1024, 16), 1, 0, 0, (1, 64, 16)),    # million-length: split into 16 segments
+    ((1, 1 << 20, 1024, 16), 1, 0, 0, (1, 64, 64)),    # million-length: 64 segments, four rounds
     ((1, 32768, 5120, 16), 1, 0, 0, (1, 64, 3)),       # 32K context: 3 x 80 tiles fill one round
     ((1, 65536, 8192, 16), 0, 0, 0, (0, 64, 1)),       # a row spans 2 GiB: 64-bit offsets
     ((2, 300, 72, 8), 0, 0, 0, (0, 64, 1)),

@@ -603,6 +603,24 @@ __global__ void __launch_bounds__(256) bwd_seg_combine_kernel(BwdArgs a, BwdWs w
   }
 }
 
+// The same composition for a few segments (at most kFoldMaxSeg): one thread per
+// (b, d, n) folds the segments' maps from the last to the first.
+constexpr int64_t kFoldMaxSeg = 8;
+__global__ void __launch_bounds__(256) bwd_seg_fold_kernel(BwdArgs a, BwdWs ws) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b, d, n)
+  if (i >= a.B * a.D * a.N) return;
+  const int64_t n = i % a.N, d = (i / a.N) % a.D, b = i / (a.N * a.D);
+  const int64_t S = ws.nseg;
+  const float Ap = a.A[d * a.N + n] * kLog2e;
+  auto slot = [&](int64_t sg) { return ((b * S + sg) * a.D + d) * a.N + n; };
+  float carry = a.dh_final ? a.dh_final[i] : 0.0f;
+  ws.carry[slot(S - 1)] = carry;
+  for (int64_t sg = S - 1; sg >= 1; --sg) {  // the adjoint leaving segment sg - 1 on the right
+    carry = fmaf(fast_exp2(Ap * ws.dsum[(b * S + sg) * a.D + d]), carry, ws.lamloc[slot(sg)]);
+    ws.carry[slot(sg - 1)] = carry;
+  }
+}
+
 // dB, dC: sum of the per-tile partials in tile order, stored in the io type.
 template <typename IO>
 __global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(BwdArgs a, BwdWs ws) {
@@ -794,7 +812,10 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
                        a, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nst = a.B * a.D * a.N;
-    hipLaunchKernelGGL(bwd_seg_combine_kernel, dim3((unsigned)((nst + 3) / 4)), dim3(256), 0, s, a, ws);
+    if (ws.nseg <= kFoldMaxSeg)
+      hipLaunchKernelGGL(bwd_seg_fold_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, a, ws);
+    else
+      hipLaunchKernelGGL(bwd_seg_combine_kernel, dim3((unsigned)((nst + 3) / 4)), dim3(256), 0, s, a, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (conv) {

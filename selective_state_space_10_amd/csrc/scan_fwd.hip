@@ -791,6 +791,25 @@ __global__ void __launch_bounds__(256) fwd_seg_combine_kernel(FwdArgs a, int64_t
   }
 }
 
+// The same composition for a few segments (at most kFoldMaxSeg): one thread per
+// (b, d, n) folds the segments' maps in order, h_in[s+1] = exp(A sum dt_s)
+// h_in[s] + hloc_s, so that no wave spends most of its lanes on absent
+// segments (accesses are coalesced along d and n).
+constexpr int64_t kFoldMaxSeg = 8;
+__global__ void __launch_bounds__(256) fwd_seg_fold_kernel(FwdArgs a, int64_t nseg) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b, d, n)
+  if (i >= a.B * a.D * a.N) return;
+  const int64_t n = i % a.N, d = (i / a.N) % a.D, b = i / (a.N * a.D);
+  const float Ap = a.A[d * a.N + n] * kLog2e;
+  auto slot = [&](int64_t sg) { return ((b * nseg + sg) * a.D + d) * a.N + n; };
+  float h = a.h0 ? a.h0[i] : 0.0f;
+  a.seg_state[slot(0)] = h;
+  for (int64_t sg = 0; sg + 1 < nseg; ++sg) {
+    h = fmaf(fast_exp2(Ap * a.seg_dsum[(b * nseg + sg) * a.D + d]), h, a.seg_hloc[slot(sg)]);
+    a.seg_state[slot(sg + 1)] = h;
+  }
+}
+
 // Sequence split for problems with too few channel tiles to fill the GPU:
 // segments of at least kMinSeg steps.  With 16 states both passes run the
 // wave-specialised kernel on 64-channel tiles, one workgroup per CU, in rounds
@@ -932,7 +951,10 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nst = a.B * a.D * a.N;
-  hipLaunchKernelGGL(fwd_seg_combine_kernel, dim3((unsigned)((nst + 3) / 4)), dim3(256), 0, s, a, nseg);
+  if (nseg <= kFoldMaxSeg)
+    hipLaunchKernelGGL(fwd_seg_fold_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, a, nseg);
+  else
+    hipLaunchKernelGGL(fwd_seg_combine_kernel, dim3((unsigned)((nst + 3) / 4)), dim3(256), 0, s, a, nseg);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (kWs) {  // the segments' full scans

@@ -90,6 +90,9 @@ constexpr double kMode1 = 0.23;
 
 int64_t bwd_split_len(int64_t B, int64_t L, int64_t D) {
   const int64_t tiles = B * ((D + kCPW - 1) / kCPW);
+  // beyond 16 rounds an unsplit grid wastes at most 1/16 of a round; this
+  // also keeps S * tiles far from overflow for any size the API accepts
+  if (tiles > 16 * kCUs) return 0;
   const int64_t smax = L / kMinSeg < 1024 ? L / kMinSeg : 1024;
   auto cost = [&](int64_t S) {
     auto rounds = [](int64_t w) { return (double)((w + kCUs - 1) / kCUs); };

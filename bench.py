@@ -27,6 +27,7 @@ import hashlib
 import json
 import os
 import sys
+import statistics
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -143,6 +144,7 @@ def _time_launches(fn, steps, warmup, rotate_inputs):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = [a.elapsed_time(b) for a, b in ev]
+    _time_launches.median_ms = statistics.median(per)
     return start.elapsed_time(stop) / steps, sum(per) / len(per), wall
 
 
@@ -503,6 +505,7 @@ def bench_fwd(args, idx, name, zoh=False, per_token=False, bidirectional=False, 
                        p["delta_bias"], True, None, return_final_state=want_hf, zoh=zoh)
 
     ms_step, ms_launch, wall = _time_launches(step, args.steps, args.warmup, sets)
+    ms_median = _time_launches.median_ms
     Bsz, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
     io_bytes = 4 if w.io_dtype == torch.float32 else 2
     nbytes = algorithmic_bytes_fwd(Bsz, L, D, N, io_bytes, h_final=want_hf)
@@ -532,7 +535,7 @@ def bench_fwd(args, idx, name, zoh=False, per_token=False, bidirectional=False, 
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
                      "algorithmic_bytes": nbytes,
-                     "kernel_ms": ms_launch, "source_sha": sha},
+                     "kernel_ms": ms_launch, "kernel_ms_median": ms_median, "source_sha": sha},
     }
     if bidirectional:
         line["roofline"]["note"] = ("two launches per step; algorithmic bytes are one read of "
@@ -580,6 +583,7 @@ def bench_decode(args, zoh=False):
 
     ms_step, ms_launch, wall = _time_launches(step, args.steps, args.warmup, tok)
     prewarm = _time_launches.prewarm_steps
+    ms_median = _time_launches.median_ms
     nbytes = algorithmic_bytes_decode(w.batch, w.dim, w.dstate, 2)
     achieved = nbytes / (ms_launch * 1e-3) / 1e9
 
@@ -604,6 +608,7 @@ def bench_decode(args, zoh=False):
                          "traffic": _traffic("decode-state-update" + ("-zoh" if zoh else ""),
                                              _source_sha(*SHA_FILES["decode"])),
                          "algorithmic_bytes": nbytes, "kernel_ms": ms_launch,
+                         "kernel_ms_median": ms_median,
                          "mall_resident": {"kind": "one state buffer, 64 consecutive steps",
                                            "achieved": nbytes / (ms_one * 1e-3) / 1e9,
                                            "unit": "GB/s", "kernel_ms": ms_one}}}
@@ -654,6 +659,7 @@ def bench_bwd(args, idx, name, conv=0, zoh=False):
                        p["delta_bias"], True, None, cs, dy, zoh=zoh)
 
     ms_step, ms_launch, wall = _time_launches(step, args.steps, args.warmup, [0])
+    ms_median = _time_launches.median_ms
     Bsz, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
     io = 4 if w.io_dtype == torch.float32 else 2
     # u, delta, z, dy in; du, ddelta, dz out; B, C in and dB, dC out; chunk states in; A, D,
@@ -678,6 +684,7 @@ def bench_bwd(args, idx, name, conv=0, zoh=False):
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                          "traffic": _traffic(name, _source_sha(*SHA_FILES["bwd"])),
                          "algorithmic_bytes": nbytes, "kernel_ms": ms_launch,
+                         "kernel_ms_median": ms_median,
                          **({} if conv or zoh else {"alu": _alu_floor_bwd(Bsz, L, D, N, ms_launch)})}}
 
 

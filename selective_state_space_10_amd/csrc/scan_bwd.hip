@@ -15,7 +15,9 @@
 //   - Prologue (cooperative, 16-byte or 8-byte accesses): dt, dt*u, e, u,
 //     d dt/d raw and dy*silu'(z) per (step, channel) into LDS, and B, C.
 //   - Recompute: the chunk's states and decay factors, forwards, into
-//     registers (32 steps x 2 states x 2 values per lane).
+//     registers (32 steps x 2 states x 2 values per lane; with the exact hold
+//     or the fused convolution two windows of 16 steps, each recomputed from
+//     the chunk start).
 //   - Reverse sweep in groups of 8 steps.  Each step leaves three per-lane
 //     partial sums over the lane's states in LDS (C h, lambda B, lambda a h A)
 //     and the per-state contributions to dB and dC, which are summed over
@@ -31,6 +33,8 @@
 // Long sequences with few channels are split into segments like the forward:
 // the adjoint entering a segment from the right is the composition of the
 // later segments' affine maps lambda -> exp(A sum dt) lambda + local part.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -40,6 +44,9 @@ namespace {
 
 constexpr int kCPW = 64;  // channels per workgroup (one per lane)
 constexpr int kTE = 8;    // steps per epilogue group
+// recompute windows per chunk (register window of T / windows steps)
+template <bool ZOH, bool CONV>
+constexpr int kBwdWindows = (ZOH || CONV) ? 2 : 1;
 constexpr int kXStride = 36;  // floats per channel-sum staging plane (32 values + padding)
 constexpr int kXRot = 12;     // rotation of the odd staging planes
 constexpr int kSwap1 = 0xB1;  // DPP quad_perm(1,0,3,2): value of lane ^ 1
@@ -173,6 +180,7 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
   constexpr int T = (int)kChunkLen;
   constexpr int TE = kTE;
   constexpr int NTG = T / TE;
+  static_assert(T % (kBwdWindows<ZOH, CONV> * TE) == 0, "windows must hold whole epilogue groups");
   constexpr int G = CPW / 4;            // 4-channel groups
   constexpr int IPT = T * G / NT;       // prologue items per thread
   constexpr int IPE = TE * CPW / NT;    // epilogue items per thread
@@ -471,84 +479,180 @@ __global__ void __launch_bounds__(64 * (N >= 2 ? N / 2 : 1)) bwd_kernel(BwdArgs 
     if (kc > 0) load_chunk(kc - 1);
     __syncthreads();
 
-    // Recompute the chunk's states and decay factors.  With ZOH the decay
-    // factors are formed again in the sweep instead: the exact hold's extra
-    // terms leave no room for both in registers (they would be spilled).
-    float Hh[T][NPL], Ha[ZOH ? 1 : T][NPL];
-    {
-      float h[NPL];
+    if constexpr (kBwdWindows<ZOH, CONV> == 1) {
+      // Recompute the chunk's states and decay factors.  With ZOH the decay
+      // factors are formed again in the sweep instead: the exact hold's extra
+      // terms leave no room for both in registers (they would be spilled).
+      float Hh[T][NPL], Ha[ZOH ? 1 : T][NPL];
+      {
+        float h[NPL];
 #pragma unroll
-      for (int s = 0; s < NPL; ++s) h[s] = hs[s];
+        for (int s = 0; s < NPL; ++s) h[s] = hs[s];
 #pragma unroll
-      for (int tl = 0; tl < T; ++tl) {
-        const float2 p = P[tl][lane];
-        const float4 bc = *(const float4 *)bcs(par, tl, w);
-        const float bv[2] = {bc.x, bc.y};
+        for (int tl = 0; tl < T; ++tl) {
+          const float2 p = P[tl][lane];
+          const float4 bc = *(const float4 *)bcs(par, tl, w);
+          const float bv[2] = {bc.x, bc.y};
 #pragma unroll
-        for (int s = 0; s < NPL; ++s) {
-          const float da = fast_exp2(p.x * Ap[s]);
-          const float cf = ZOH ? zoh_coef(p.x, p.x * An[s], da, Ainv[s]) : 1.0f;
-          h[s] = fmaf(da, h[s], ZOH ? cf * p.y * bv[s] : p.y * bv[s]);
-          Hh[tl][s] = h[s];
-          if (!ZOH) Ha[ZOH ? 0 : tl][s] = da;
-        }
-      }
-    }
-
-#pragma unroll
-    for (int tg = NTG - 1; tg >= 0; --tg) {
-#pragma unroll
-      for (int tq = TE - 1; tq >= 0; --tq) {
-        const int tl = tg * TE + tq;
-        const float2 p = P[tl][lane];
-        const float e = E[tl][lane];
-        const float4 bc = *(const float4 *)bcs(par, tl, w);
-        const float bv[2] = {bc.x, bc.y};
-        const float cv[2] = {NPL == 2 ? bc.z : bc.y, bc.w};
-        float pre = 0.0f, dup = 0.0f, ddp = 0.0f, cB[NPL], cC[NPL];
-#pragma unroll
-        for (int s = 0; s < NPL; ++s) {
-          const float ht = Hh[tl][s];
-          const float hp = tl > 0 ? Hh[tl > 0 ? tl - 1 : 0][s] : hs[s];
-          const float lt = fmaf(e, cv[s], lam[s]);
-          const float da = ZOH ? fast_exp2(p.x * Ap[s]) : Ha[ZOH ? 0 : tl][s];
-          pre = fmaf(cv[s], ht, pre);
-          cC[s] = e * ht;
-          lam[s] = da * lt;
-          const float r = lam[s] * hp;
-          ddp = fmaf(r, An[s], ddp);
-          dAacc[s] = fmaf(r, p.x, dAacc[s]);
-          if (ZOH) {  // p.y is u; the coefficient and its derivatives enter every term
-            const float x = p.x * An[s];
-            const float cf = zoh_coef(p.x, x, da, Ainv[s]);
-            const float lu = lt * p.y;
-            cB[s] = lu * cf;
-            dup = fmaf(lt * cf, bv[s], dup);
-            const float q = lu * bv[s];
-            ddp = fmaf(q, da, ddp);
-            dAacc[s] = fmaf(q, zoh_dcoef_dA(p.x, x, da, cf, Ainv[s]), dAacc[s]);
-          } else {  // p.y is dt*u
-            cB[s] = lt * p.y;
-            dup = fmaf(lt, bv[s], dup);
+          for (int s = 0; s < NPL; ++s) {
+            const float da = fast_exp2(p.x * Ap[s]);
+            const float cf = ZOH ? zoh_coef(p.x, p.x * An[s], da, Ainv[s]) : 1.0f;
+            h[s] = fmaf(da, h[s], ZOH ? cf * p.y * bv[s] : p.y * bv[s]);
+            Hh[tl][s] = h[s];
+            if (!ZOH) Ha[ZOH ? 0 : tl][s] = da;
           }
         }
-        Q[0][tq][w][lane] = pre;
-        Q[1][tq][w][lane] = dup;
-        Q[2][tq][w][lane] = ddp;
-        if constexpr (NPL == 2) {
-          const int xi = ((lane >> 1) + kXRot * par) & 31;
-          X[w][tq][par][xi] = cB[0] + dpp_mov<kSwap1>(cB[1]);
-          X[w][tq][2 + par][xi] = cC[0] + dpp_mov<kSwap1>(cC[1]);
-        } else {
-          const int xi = ((lane & 31) + kXRot * (lane >> 5)) & 31;
-          X[w][tq][lane >> 5][xi] = cB[0];
-          X[w][tq][2 + (lane >> 5)][xi] = cC[0];
-        }
       }
-      __syncthreads();
-      epilogue(kc, tg);
-      channel_sums(kc, tg);
-      __syncthreads();
+
+#pragma unroll
+      for (int tg = NTG - 1; tg >= 0; --tg) {
+#pragma unroll
+        for (int tq = TE - 1; tq >= 0; --tq) {
+          const int tl = tg * TE + tq;
+          const float2 p = P[tl][lane];
+          const float e = E[tl][lane];
+          const float4 bc = *(const float4 *)bcs(par, tl, w);
+          const float bv[2] = {bc.x, bc.y};
+          const float cv[2] = {NPL == 2 ? bc.z : bc.y, bc.w};
+          float pre = 0.0f, dup = 0.0f, ddp = 0.0f, cB[NPL], cC[NPL];
+#pragma unroll
+          for (int s = 0; s < NPL; ++s) {
+            const float ht = Hh[tl][s];
+            const float hp = tl > 0 ? Hh[tl > 0 ? tl - 1 : 0][s] : hs[s];
+            const float lt = fmaf(e, cv[s], lam[s]);
+            const float da = ZOH ? fast_exp2(p.x * Ap[s]) : Ha[ZOH ? 0 : tl][s];
+            pre = fmaf(cv[s], ht, pre);
+            cC[s] = e * ht;
+            lam[s] = da * lt;
+            const float r = lam[s] * hp;
+            ddp = fmaf(r, An[s], ddp);
+            dAacc[s] = fmaf(r, p.x, dAacc[s]);
+            if (ZOH) {  // p.y is u; the coefficient and its derivatives enter every term
+              const float x = p.x * An[s];
+              const float cf = zoh_coef(p.x, x, da, Ainv[s]);
+              const float lu = lt * p.y;
+              cB[s] = lu * cf;
+              dup = fmaf(lt * cf, bv[s], dup);
+              const float q = lu * bv[s];
+              ddp = fmaf(q, da, ddp);
+              dAacc[s] = fmaf(q, zoh_dcoef_dA(p.x, x, da, cf, Ainv[s]), dAacc[s]);
+            } else {  // p.y is dt*u
+              cB[s] = lt * p.y;
+              dup = fmaf(lt, bv[s], dup);
+            }
+          }
+          Q[0][tq][w][lane] = pre;
+          Q[1][tq][w][lane] = dup;
+          Q[2][tq][w][lane] = ddp;
+          if constexpr (NPL == 2) {
+            const int xi = ((lane >> 1) + kXRot * par) & 31;
+            X[w][tq][par][xi] = cB[0] + dpp_mov<kSwap1>(cB[1]);
+            X[w][tq][2 + par][xi] = cC[0] + dpp_mov<kSwap1>(cC[1]);
+          } else {
+            const int xi = ((lane & 31) + kXRot * (lane >> 5)) & 31;
+            X[w][tq][lane >> 5][xi] = cB[0];
+            X[w][tq][2 + (lane >> 5)][xi] = cC[0];
+          }
+        }
+        __syncthreads();
+        epilogue(kc, tg);
+        channel_sums(kc, tg);
+        __syncthreads();
+      }
+    } else {
+      // The same recompute and sweep in two windows of T/2 steps, the later
+      // one first, each recomputed from the chunk start.  A 32-step window
+      // spills with the exact hold's or the convolution's extra registers; the
+      // extra recompute costs less than the spill (about 3% of the call).  The
+      // plain variant keeps the one-window code above: written in this generic
+      // form its register allocation gets worse.
+      auto run_window = [&](auto window) {
+        constexpr int WI = decltype(window)::value;  // window index, later first
+        constexpr int TW = T / kBwdWindows<ZOH, CONV>;
+        constexpr int T0 = WI * TW;  // first step of the window
+        float Hh[TW][NPL], Ha[ZOH ? 1 : TW][NPL], hm[NPL];  // hm: state before step T0
+        {
+          float h[NPL];
+#pragma unroll
+          for (int s = 0; s < NPL; ++s) h[s] = hs[s], hm[s] = hs[s];
+#pragma unroll
+          for (int tl = 0; tl < T0 + TW; ++tl) {
+            const float2 p = P[tl][lane];
+            const float4 bc = *(const float4 *)bcs(par, tl, w);
+            const float bv[2] = {bc.x, bc.y};
+#pragma unroll
+            for (int s = 0; s < NPL; ++s) {
+              const float da = fast_exp2(p.x * Ap[s]);
+              const float cf = ZOH ? zoh_coef(p.x, p.x * An[s], da, Ainv[s]) : 1.0f;
+              h[s] = fmaf(da, h[s], ZOH ? cf * p.y * bv[s] : p.y * bv[s]);
+              if (tl == T0 - 1) hm[s] = h[s];
+              if (tl >= T0) {
+                Hh[tl >= T0 ? tl - T0 : 0][s] = h[s];
+                if (!ZOH) Ha[(ZOH || tl < T0) ? 0 : tl - T0][s] = da;
+              }
+            }
+          }
+        }
+
+#pragma unroll
+        for (int tg = (T0 + TW) / TE - 1; tg >= T0 / TE; --tg) {
+#pragma unroll
+          for (int tq = TE - 1; tq >= 0; --tq) {
+            const int tl = tg * TE + tq;
+            const int ti = tl - T0;  // step within the window
+            const float2 p = P[tl][lane];
+            const float e = E[tl][lane];
+            const float4 bc = *(const float4 *)bcs(par, tl, w);
+            const float bv[2] = {bc.x, bc.y};
+            const float cv[2] = {NPL == 2 ? bc.z : bc.y, bc.w};
+            float pre = 0.0f, dup = 0.0f, ddp = 0.0f, cB[NPL], cC[NPL];
+#pragma unroll
+            for (int s = 0; s < NPL; ++s) {
+              const float ht = Hh[ti][s];
+              const float hp = ti > 0 ? Hh[ti > 0 ? ti - 1 : 0][s] : hm[s];
+              const float lt = fmaf(e, cv[s], lam[s]);
+              const float da = ZOH ? fast_exp2(p.x * Ap[s]) : Ha[ZOH ? 0 : ti][s];
+              pre = fmaf(cv[s], ht, pre);
+              cC[s] = e * ht;
+              lam[s] = da * lt;
+              const float r = lam[s] * hp;
+              ddp = fmaf(r, An[s], ddp);
+              dAacc[s] = fmaf(r, p.x, dAacc[s]);
+              if (ZOH) {  // p.y is u; the coefficient and its derivatives enter every term
+                const float x = p.x * An[s];
+                const float cf = zoh_coef(p.x, x, da, Ainv[s]);
+                const float lu = lt * p.y;
+                cB[s] = lu * cf;
+                dup = fmaf(lt * cf, bv[s], dup);
+                const float q = lu * bv[s];
+                ddp = fmaf(q, da, ddp);
+                dAacc[s] = fmaf(q, zoh_dcoef_dA(p.x, x, da, cf, Ainv[s]), dAacc[s]);
+              } else {  // p.y is dt*u
+                cB[s] = lt * p.y;
+                dup = fmaf(lt, bv[s], dup);
+              }
+            }
+            Q[0][tq][w][lane] = pre;
+            Q[1][tq][w][lane] = dup;
+            Q[2][tq][w][lane] = ddp;
+            if constexpr (NPL == 2) {
+              const int xi = ((lane >> 1) + kXRot * par) & 31;
+              X[w][tq][par][xi] = cB[0] + dpp_mov<kSwap1>(cB[1]);
+              X[w][tq][2 + par][xi] = cC[0] + dpp_mov<kSwap1>(cC[1]);
+            } else {
+              const int xi = ((lane & 31) + kXRot * (lane >> 5)) & 31;
+              X[w][tq][lane >> 5][xi] = cB[0];
+              X[w][tq][2 + (lane >> 5)][xi] = cC[0];
+            }
+          }
+          __syncthreads();
+          epilogue(kc, tg);
+          channel_sums(kc, tg);
+          __syncthreads();
+        }
+      };
+      run_window(std::integral_constant<int, 1>{});
+      run_window(std::integral_constant<int, 0>{});
     }
   }
 

@@ -750,11 +750,9 @@ constexpr int kWsSteps = 16, kWsRing = 2;
 template <typename IO, int CPW, int MODE, bool ZOH>
 static void launch_ws(const FwdArgs &a, dim3 grid, hipStream_t s) {
   const dim3 block(64 * (CPW / 8 + CPW / 16));
-  if constexpr (CPW != 80) {  // not instantiated on 80-channel tiles, which the launcher never gives it
-    if (a.conv_k) {
-      hipLaunchKernelGGL((fwd_ws_kernel<IO, CPW, kWsSteps, kWsRing, true, MODE, ZOH, true>), grid, block, 0, s, a);
-      return;
-    }
+  if (a.conv_k) {
+    hipLaunchKernelGGL((fwd_ws_kernel<IO, CPW, kWsSteps, kWsRing, true, MODE, ZOH, true>), grid, block, 0, s, a);
+    return;
   }
   if (a.flags)
     hipLaunchKernelGGL((fwd_ws_kernel<IO, CPW, kWsSteps, kWsRing, true, MODE, ZOH, false>), grid, block, 0, s, a);
@@ -886,7 +884,7 @@ static int device_cus() {
 }
 
 template <int N>
-static int pick_cpw(const FwdArgs &a) {
+static int pick_cpw(const FwdArgs &a, int64_t io_bytes) {
   static const int env = [] {
     const char *e = getenv("SSM_FWD_CPW");
     return e ? atoi(e) : 0;
@@ -906,14 +904,20 @@ static int pick_cpw(const FwdArgs &a) {
     // a CU holding two 32-channel workgroups costs 83 and one alone 35
     // (measured on MI355X: 16 x 2048 x 2048 fp32 takes 331 us on 64-channel
     // tiles, 372 on 80, 400 on 32; 12 x 2048 x 2048 takes 285 on 32, 289 on
-    // 64; 8 x 4096 x 5120 bf16 takes 710 on 80, 795 on 64, 905 on 32).  The
-    // fused convolution has no 80-channel variant.
+    // 64; 8 x 4096 x 5120 bf16 takes 710 on 80, 795 on 64, 905 on 32).  With
+    // the fused convolution in fp32 the 80- and 32-channel variants spill
+    // registers (their x rows in flight are 16-byte values): a round of 80
+    // costs 102 (4 x 4096 x 5120: 0.557 ms on 80 in one round, 0.693 ms on 64
+    // in two), and 32-channel tiles are never the fastest (1.10 ms there;
+    // 12 x 2048 x 2040: 0.58 ms on 32, 0.38 on 64).  In bf16 the costs above
+    // hold with the convolution too.
     auto rounds = [&](int64_t wg) { return (wg + cus - 1) / cus; };
+    const bool conv_f32 = a.conv_k != 0 && io_bytes == 4;
     const int64_t wg32 = a.B * ((a.D + 31) / 32);
     const int64_t full = wg32 / (2 * cus), rest = wg32 % (2 * cus);
-    const int64_t c32 = full * 83 + (rest == 0 ? 0 : rest > cus ? 83 : 35);
+    const int64_t c32 = conv_f32 ? INT64_MAX : full * 83 + (rest == 0 ? 0 : rest > cus ? 83 : 35);
     const int64_t c64 = rounds(wg64) * 64;
-    const int64_t c80 = a.conv_k ? INT64_MAX : rounds(a.B * ((a.D + 79) / 80)) * 80;
+    const int64_t c80 = rounds(a.B * ((a.D + 79) / 80)) * (conv_f32 ? 102 : 80);
     if (c64 <= c80 && c64 <= c32) return 64;
     return c80 <= c32 ? 80 : 32;
   }
@@ -982,8 +986,7 @@ static FwdPlan plan_fwd_t(const FwdArgs &a, int64_t io_bytes) {
     // 16 states, no sequence split, and every row of a (B,L,D) array within
     // 32-bit offsets: the wave-specialised kernel, also for the options
     pl.kernel = kPlanWaveSpecialised;
-    int cpw = pick_cpw<N>(a);
-    if (cpw == 80 && a.conv_k) cpw = 32;  // the convolution variant needs more than 128 registers
+    int cpw = pick_cpw<N>(a, io_bytes);
     if (cpw == 16) cpw = 32;              // (a tuning override; 32 is the narrowest tile here)
     pl.tile_channels = cpw;
     return pl;
@@ -992,7 +995,7 @@ static FwdPlan plan_fwd_t(const FwdArgs &a, int64_t io_bytes) {
   if (a.flags || a.conv_k) {
     cpw = OCPW;
   } else {
-    const int c = pick_cpw<N>(a);
+    const int c = pick_cpw<N>(a, io_bytes);
     cpw = (mincpw <= 16 && c == 16) ? 16 : (mincpw <= 32 && c == 32) ? 32 : 64;
   }
   if (N == 16 && pl.segment_len) {  // both passes of a split: the wave-specialised kernel, 64-channel tiles

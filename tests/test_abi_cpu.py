@@ -195,14 +195,17 @@ ZOH, REV, TOK, ACC = 1, 2, 4, 8
     ((8, 2048, 2048, 16), 0, 0, 0, (1, 64, 1)),        # Mamba-370m layer: 256 tiles of 64
     ((8, 2048, 2048, 16), 0, ZOH, 4, (1, 64, 1)),
     ((4, 4096, 5120, 16), 1, 0, 0, (1, 80, 1)),        # Mamba-2.8b layer: 256 tiles of 80
-    ((4, 4096, 5120, 16), 1, 0, 4, (1, 32, 1)),        # ... with the fused convolution
+    ((4, 4096, 5120, 16), 1, 0, 4, (1, 80, 1)),        # ... with the fused convolution too
+    ((4, 4096, 5120, 16), 0, 0, 4, (1, 80, 1)),        # fp32 with the convolution: 80 costs 102
     ((12, 40, 2040, 16), 0, 0, 0, (1, 32, 1)),         # 1.5 rounds of 32-channel tiles
     ((12, 40, 2040, 16), 1, ZOH, 0, (1, 32, 1)),
     ((12, 40, 2040, 16), 0, REV | TOK, 0, (1, 32, 1)),
-    ((12, 40, 2040, 16), 0, 0, 4, (1, 32, 1)),
+    ((12, 40, 2040, 16), 1, 0, 4, (1, 32, 1)),
+    ((12, 40, 2040, 16), 0, 0, 4, (1, 64, 1)),         # fp32 with the convolution: never 32
     ((16, 24, 2048, 16), 0, 0, 0, (1, 64, 1)),         # two full rounds of 64-channel tiles
     ((8, 4096, 5120, 16), 1, 0, 0, (1, 80, 1)),        # two full rounds of 80-channel tiles
-    ((8, 4096, 5120, 16), 1, 0, 4, (1, 64, 1)),        # ... no 80 with the convolution
+    ((8, 4096, 5120, 16), 1, 0, 4, (1, 80, 1)),        # ... and with the convolution
+    ((8, 4096, 5120, 16), 0, 0, 4, (1, 64, 1)),        # fp32: 3 rounds of 64 beat 2 of 80
     ((8, 40, 3336, 16), 0, 0, 0, (1, 64, 1)),          # 424 tiles of 64: two rounds beat 32
     ((1, 37, 20480, 16), 0, 0, 0, (1, 80, 1)),
     ((1, 1 << 20, 1024, 16), 1, 0, 0, (1, 64, 64)),    # million-length: 64 segments, four rounds

@@ -158,20 +158,22 @@ def _conv_slice(p, cw, cb, sel):
                 delta_bias=p["delta_bias"][s].cpu(), delta_softplus=True, h0=None)
 
 
-# channels at both ends of 32-channel tiles, both halves of a tile's state
-# slices, and the last channel
-_SEL_2P8B = torch.tensor([0, 1, 31, 32, 63, 64, 1999, 2048, 2559, 4095, 5088, 5119])
+# channels at both ends of the forward's 80-channel tiles and of the
+# backward's 64-channel tiles, both lane parities, and the last channel
+_SEL_2P8B = torch.tensor([0, 1, 63, 64, 79, 80, 159, 160, 1999, 2048, 2559, 2560, 4095, 5039, 5040,
+                          5119])
 
 
 def test_fwd_conv_workload2_full_size(ssm):
     """The Mamba-2.8b layer shape (4 x 4096 x 5120, bf16) with a width-4
     convolution, in the launch configuration the forward picks there (the
-    wave-specialised kernel on 32-channel tiles), on sampled channels."""
+    wave-specialised kernel on 80-channel tiles, one round), on sampled
+    channels."""
     w = WORKLOADS[2]
     p = workload_inputs(2, device="cuda")
     cw, cb = conv_inputs(w.dim, 4, seed=2, device="cuda")
     plan = ssm.scan_fwd_plan(w.batch, w.seqlen, w.dim, w.dstate, w.io_dtype, conv_width=4)
-    assert (plan["kernel"], plan["tile_channels"], plan["segments"]) == ("wave-specialised", 32, 1)
+    assert (plan["kernel"], plan["tile_channels"], plan["segments"]) == ("wave-specialised", 80, 1)
     y, hf, cs = ssm.scan_fwd_conv(p["u"], cw, cb, p["delta"], p["A"], p["B"], p["C"], p["D"],
                                   p["z"], p["delta_bias"], True, None, return_final_state=True,
                                   save_chunk_states=True)

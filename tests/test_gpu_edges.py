@@ -91,12 +91,36 @@ def test_many_channel_tiles(ssm, dtype, opts):
 @pytest.mark.parametrize("opts", [dict(), dict(zoh=True, tok=True)], ids=["plain", "zoh-per-token"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_many_channel_tiles_fused_conv(ssm, dtype, opts):
-    """The fused convolution on 32-channel tiles (12 x 64 tiles), against the
-    oracle's convolution followed by its scan."""
+    """The fused convolution at 12 x 2040 channels: on 32-channel tiles (12 x 64
+    tiles) in bf16, on 64-channel tiles in fp32 (whose 32-channel variant is
+    never the fastest), against the oracle's convolution followed by its scan."""
     from tests.test_gpu_conv import _conv_problem, _gpu_fwd as _conv_fwd, _okw
     zoh = opts.get("zoh", False)
     p = _conv_problem(12, 40, 2040, 16, dtype, 4, seed=47, tok=opts.get("tok", False))
-    _assert_plan(ssm, p, 32, zoh=zoh, conv=4)
+    _assert_plan(ssm, p, 32 if dtype == torch.bfloat16 else 64, zoh=zoh, conv=4)
+    T = ssm.chunk_len()
+    y, hf, cs = _conv_fwd(ssm, _to(p, "cuda"), zoh, return_final_state=True, save_chunk_states=True)
+    torch.cuda.synchronize()
+    yo, hfo, cso = oracle_c.scan_fwd_conv(**_okw(p), chunk_len=T, zoh=zoh)
+    assert nmax_err(y, yo) <= TOL[dtype]
+    assert nmax_err(hf, hfo) <= TOL[dtype]
+    assert nmax_err(cs.permute(0, 1, 3, 2), cso) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("opts", [dict(), dict(zoh=True, tok=True, bias=False)],
+                         ids=["plain", "zoh-per-token-no-bias"])
+@pytest.mark.parametrize("D,dtype", [(5120, torch.float32), (5120, torch.bfloat16),
+                                     (5112, torch.bfloat16)], ids=["5120-f32", "5120-bf16", "5112-bf16"])
+def test_eighty_channel_tiles_fused_conv(ssm, D, dtype, opts):
+    """The fused convolution on 80-channel tiles (4 rows of 5120 or 5112
+    channels: one round of 64 or 65 tiles per row over 256 compute units, where
+    64-channel tiles would need two), the last tile ragged for 5112, against the
+    oracle's convolution followed by its scan."""
+    from tests.test_gpu_conv import _conv_problem, _gpu_fwd as _conv_fwd, _okw
+    opts = dict(opts)
+    zoh = opts.pop("zoh", False)
+    p = _conv_problem(4, 48, D, 16, dtype, 4, seed=D % 97, **opts)
+    _assert_plan(ssm, p, 80, zoh=zoh, conv=4)
     T = ssm.chunk_len()
     y, hf, cs = _conv_fwd(ssm, _to(p, "cuda"), zoh, return_final_state=True, save_chunk_states=True)
     torch.cuda.synchronize()

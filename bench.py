@@ -12,6 +12,7 @@ line (rank 0).
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 ``--workload`` also accepts the other shapes and options (mamba-2.8b-layer-fwd,
+the same with the fused width-4 convolution (mamba-2.8b-layer-fwd-conv4),
 the 32K-context forward at the 2.8b width (mamba-2.8b-32k-fwd),
 decode-state-update, million-length-fwd, million-length-bwd,
 mamba-370m-layer-bwd, the 370m forward with the exact zero-order hold, with one
@@ -47,7 +48,7 @@ WORKLOAD_NAMES = ["mamba-370m-layer-fwd", "mamba-2.8b-layer-fwd", "decode-state-
                   "mamba-370m-layer-fwd-zoh", "mamba-370m-layer-fwd-token-delta",
                   "mamba-370m-layer-bidirectional", "decode-state-update-zoh",
                   "mamba-370m-layer-fwd-conv4", "mamba-370m-layer-bwd-conv4", "mamba-370m-layer-bwd-zoh",
-                  "mamba-2.8b-32k-fwd"]
+                  "mamba-2.8b-32k-fwd", "mamba-2.8b-layer-fwd-conv4"]
 METRIC = "selective-scan fwd tokens·channels/s and HBM GB/s (% of peak), Mamba-370m shape"
 # The only throughput figure the source pages give for the method is relative and
 # names no hardware, precision or workload: context beside the kernel's rate, not
@@ -730,6 +731,8 @@ def main():
         line = bench_bwd(args, 1, wl)
     elif wl == "mamba-370m-layer-fwd-conv4":
         line = bench_fwd(args, 1, wl, conv=4)
+    elif wl == "mamba-2.8b-layer-fwd-conv4":
+        line = bench_fwd(args, 2, wl, conv=4)
     elif wl == "mamba-370m-layer-bwd-conv4":
         line = bench_bwd(args, 1, wl, conv=4)
     elif wl == "mamba-370m-layer-bwd-zoh":

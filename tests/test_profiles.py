@@ -29,7 +29,7 @@ with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
 
 
 def _kind(name):
-    return "decode" if name.startswith("decode") else "bwd" if name.endswith("-bwd") else "fwd"
+    return "decode" if name.startswith("decode") else "bwd" if "-bwd" in name else "fwd"
 
 
 @pytest.mark.parametrize("name", sorted(TRAFFIC))

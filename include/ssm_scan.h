@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSM_SCAN_ABI_VERSION 3
+#define SSM_SCAN_ABI_VERSION 4
 
 typedef enum ssm_status {
   SSM_OK = 0,
@@ -140,6 +140,10 @@ typedef struct ssm_fwd_plan {
   int32_t tile_channels; /* channels per workgroup: 16, 32, 64 or 80 */
   int64_t segments;      /* sequence segments (1 = no split) */
   int64_t segment_len;   /* steps per segment (0 = no split) */
+  int64_t first_pass_len; /* steps per piece of a split's first pass, which
+                             finds the end state of every segment but the
+                             last in segment_len / first_pass_len pieces
+                             (0 = no split) */
 } ssm_fwd_plan;
 
 int ssm_scan_fwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,

@@ -22,7 +22,8 @@ class FwdPlan(ctypes.Structure):
     """ssm_fwd_plan: kernel (0 all-purpose, 1 wave-specialised), channels per
     workgroup, sequence segments and their length."""
     _fields_ = [("kernel", ctypes.c_int32), ("tile_channels", ctypes.c_int32),
-                ("segments", ctypes.c_int64), ("segment_len", ctypes.c_int64)]
+                ("segments", ctypes.c_int64), ("segment_len", ctypes.c_int64),
+                ("first_pass_len", ctypes.c_int64)]
 
 # option bits of the *_ex entry points
 FLAG_ZOH = 1

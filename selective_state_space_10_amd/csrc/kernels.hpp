@@ -81,6 +81,7 @@ struct FwdPlan {
   int tile_channels;
   int64_t segments;     // 1 = no sequence split
   int64_t segment_len;  // steps per segment (0 = no split)
+  int64_t first_pass_len;  // steps per piece of the split's first pass (0 = no split)
 };
 FwdPlan plan_fwd(const FwdArgs &a, int io_dtype);
 

@@ -762,49 +762,59 @@ static void launch_ws(const FwdArgs &a, dim3 grid, hipStream_t s) {
 
 // Second phase of a sequence split: the state entering every segment,
 // h_in[0] = h0, h_in[s+1] = exp(A * sum of dt over s) * h_in[s] + h_loc[s],
-// i.e. an exclusive scan of the segments' affine maps.  One wave per (b, d, n),
-// segments on the lanes (64 at a time), composed by the wave-wide associative
-// scan; the state is carried from one piece of 64 segments to the next.
-__global__ void __launch_bounds__(256) fwd_seg_combine_kernel(FwdArgs a, int64_t nseg) {
+// i.e. an exclusive scan of the segments' affine maps.  The first pass may have
+// cut each segment into `pieces` pieces: then the maps composed are the
+// pieces' ((nseg - 1) * pieces of them; their end states and step-size sums
+// have rows of nrow pieces), and the state after every pieces-th one is the
+// start state of a segment.  One wave per (b, d, n), pieces on the lanes (64
+// at a time), composed by the wave-wide associative scan; the state is carried
+// from one group of 64 to the next.
+__global__ void __launch_bounds__(256) fwd_seg_combine_kernel(FwdArgs a, int64_t nseg, int64_t pieces,
+                                                               int64_t nrow) {
   const int lane = threadIdx.x & 63;
   const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, d, n): uniform over the wave
   if (i >= a.B * a.D * a.N) return;
   const int64_t n = i % a.N, d = (i / a.N) % a.D, b = i / (a.N * a.D);
   const float Ap = a.A[d * a.N + n] * kLog2e;
-  auto slot = [&](int64_t sg) { return ((b * nseg + sg) * a.D + d) * a.N + n; };
+  auto slot = [&](int64_t sg) { return ((b * nseg + sg) * a.D + d) * a.N + n; };   // segment starts
+  auto pslot = [&](int64_t pc) { return ((b * nrow + pc) * a.D + d) * a.N + n; };  // piece end states
+  const int64_t nmap = (nseg - 1) * pieces;
   float carry = a.h0 ? a.h0[i] : 0.0f;
   if (lane == 0) a.seg_state[slot(0)] = carry;
-  for (int64_t s0 = 0; s0 + 1 < nseg; s0 += 64) {
-    const int64_t sg = s0 + lane;  // the segment whose map this lane holds
-    const bool valid = sg + 1 < nseg;
+  for (int64_t s0 = 0; s0 < nmap; s0 += 64) {
+    const int64_t pc = s0 + lane;  // the piece whose map this lane holds
+    const bool valid = pc < nmap;
     float x = 1.0f, y = 0.0f;      // identity past the last map
     if (valid) {
-      x = fast_exp2(Ap * a.seg_dsum[(b * nseg + sg) * a.D + d]);
-      y = a.seg_hloc[slot(sg)];
+      x = fast_exp2(Ap * a.seg_dsum[(b * nrow + pc) * a.D + d]);
+      y = a.seg_hloc[pslot(pc)];
     }
     wave_affine_scan(x, y);
-    const float h = fmaf(x, carry, y);  // the state entering segment sg + 1
-    if (valid) a.seg_state[slot(sg + 1)] = h;
+    const float h = fmaf(x, carry, y);  // the state after piece pc
+    if (valid && (pc + 1) % pieces == 0) a.seg_state[slot((pc + 1) / pieces)] = h;
     carry = __shfl(h, 63, 64);
   }
 }
 
-// The same composition for a few segments (at most kFoldMaxSeg): one thread per
-// (b, d, n) folds the segments' maps in order, h_in[s+1] = exp(A sum dt_s)
-// h_in[s] + hloc_s, so that no wave spends most of its lanes on absent
-// segments (accesses are coalesced along d and n).
+// The same composition for a few maps (at most kFoldMaxSeg): one thread per
+// (b, d, n) folds the pieces' maps in order, h <- exp(A sum dt_p) h + hloc_p,
+// so that no wave spends most of its lanes on absent maps (accesses are
+// coalesced along d and n).
 constexpr int64_t kFoldMaxSeg = 8;
-__global__ void __launch_bounds__(256) fwd_seg_fold_kernel(FwdArgs a, int64_t nseg) {
+__global__ void __launch_bounds__(256) fwd_seg_fold_kernel(FwdArgs a, int64_t nseg, int64_t pieces,
+                                                            int64_t nrow) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b, d, n)
   if (i >= a.B * a.D * a.N) return;
   const int64_t n = i % a.N, d = (i / a.N) % a.D, b = i / (a.N * a.D);
   const float Ap = a.A[d * a.N + n] * kLog2e;
   auto slot = [&](int64_t sg) { return ((b * nseg + sg) * a.D + d) * a.N + n; };
+  auto pslot = [&](int64_t pc) { return ((b * nrow + pc) * a.D + d) * a.N + n; };
   float h = a.h0 ? a.h0[i] : 0.0f;
   a.seg_state[slot(0)] = h;
-  for (int64_t sg = 0; sg + 1 < nseg; ++sg) {
-    h = fmaf(fast_exp2(Ap * a.seg_dsum[(b * nseg + sg) * a.D + d]), h, a.seg_hloc[slot(sg)]);
-    a.seg_state[slot(sg + 1)] = h;
+  const int64_t nmap = (nseg - 1) * pieces;
+  for (int64_t pc = 0; pc < nmap; ++pc) {
+    h = fmaf(fast_exp2(Ap * a.seg_dsum[(b * nrow + pc) * a.D + d]), h, a.seg_hloc[pslot(pc)]);
+    if ((pc + 1) % pieces == 0) a.seg_state[slot((pc + 1) / pieces)] = h;
   }
 }
 
@@ -863,6 +873,32 @@ static int64_t split_len(int64_t B, int64_t L, int64_t D, int64_t N, int64_t io_
   // (D < 8192 here, so the cap is at least 65472 steps)
   const int64_t cap = ws_max_rows(D, io_bytes) / kChunkLen * kChunkLen;
   return len < cap ? len : cap;
+}
+
+// Steps per piece of a split's first pass (16 states).  The first pass runs on
+// the S - 1 segments before the last, and with few channel tiles it leaves CUs
+// idle (at the 32K-context shape 2 x 80 workgroups on 256 CUs).  Cut into k
+// pieces of len / k steps (a multiple of kChunkLen, at least kMinPiece), it
+// runs R((S - 1) k tiles) rounds of pieces k times shorter; the smallest k with
+// the fewest such rounds per unit of length is taken if that saves at least 5%
+// (k = 1 where no cut helps, as at the million-length shape).  Pieces are kept
+// long enough that a workgroup's start (its first loads in flight) stays a
+// small part of its time.  Depends on sizes only.
+constexpr int64_t kMinPiece = 2048;
+static int64_t piece_len(int64_t B, int64_t L, int64_t D, int64_t N, int64_t io_bytes) {
+  const int64_t len = split_len(B, L, D, N, io_bytes);
+  if (len == 0 || N != 16) return len;
+  const int64_t nseg = (L + len - 1) / len;
+  const int64_t first = (nseg - 1) * B * ((D + 63) / 64);  // first-pass workgroups, uncut
+  auto rounds = [](int64_t w) { return (double)((w + kSplitCUs - 1) / kSplitCUs); };
+  int64_t best_k = 1;
+  double best = rounds(first);
+  for (int64_t k = 2; len / k >= kMinPiece && k <= 64; ++k) {
+    if (len % (k * kChunkLen) != 0) continue;
+    const double c = rounds(k * first) / (double)k;
+    if (c < best * 0.95) best = c, best_k = k;
+  }
+  return len / best_k;
 }
 
 // Channels per workgroup (CPW) for dstate N.  A 64-channel tile takes a CU
@@ -940,25 +976,33 @@ static hipError_t launch_fwd_cpw(const FwdArgs &a0, hipStream_t s) {
     return hipGetLastError();
   }
   const int64_t nseg = (a.L + a.seg_len - 1) / a.seg_len;
+  // the first pass's pieces: pieces per segment, and rows of pieces over the
+  // whole length (the layout of their end states and step-size sums)
+  const int64_t plen = piece_len(a.B, a.L, a.D, a.N, sizeof(IO));
+  const int64_t pieces = a.seg_len / plen, nrow = (a.L + plen - 1) / plen;
   float *ws = (float *)a.workspace;
   a.seg_hloc = ws;
-  a.seg_state = ws + a.B * nseg * a.D * a.N;
-  a.seg_dsum = ws + 2 * a.B * nseg * a.D * a.N;
+  a.seg_state = ws + a.B * nrow * a.D * a.N;
+  a.seg_dsum = a.seg_state + a.B * nseg * a.D * a.N;
   // 16 states: both passes run the wave-specialised kernel on 64-channel tiles
   constexpr bool kWs = N == 16;
   const unsigned t64 = (unsigned)((a.D + 63) / 64);
-  if constexpr (kWs)
-    launch_ws<IO, 64, 1, ZOH>(a, dim3(t64, (unsigned)a.B, (unsigned)(nseg - 1)), s);
-  else
+  if constexpr (kWs) {
+    FwdArgs a1 = a;  // the first pass over pieces of plen steps
+    a1.seg_len = plen;
+    launch_ws<IO, 64, 1, ZOH>(a1, dim3(t64, (unsigned)a.B, (unsigned)((nseg - 1) * pieces)), s);
+  } else {
     hipLaunchKernelGGL((fwd_kernel<IO, N, NPL, CPW, T, PD, 1, ZOH, FLAGS>), dim3(tiles, (unsigned)a.B, (unsigned)(nseg - 1)),
                        dim3(64 * NW), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nst = a.B * a.D * a.N;
-  if (nseg <= kFoldMaxSeg)
-    hipLaunchKernelGGL(fwd_seg_fold_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, a, nseg);
+  if ((nseg - 1) * pieces <= kFoldMaxSeg)
+    hipLaunchKernelGGL(fwd_seg_fold_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, s, a, nseg, pieces, nrow);
   else
-    hipLaunchKernelGGL(fwd_seg_combine_kernel, dim3((unsigned)((nst + 3) / 4)), dim3(256), 0, s, a, nseg);
+    hipLaunchKernelGGL(fwd_seg_combine_kernel, dim3((unsigned)((nst + 3) / 4)), dim3(256), 0, s, a, nseg, pieces,
+                       nrow);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (kWs) {  // the segments' full scans
@@ -982,6 +1026,7 @@ static FwdPlan plan_fwd_t(const FwdArgs &a, int64_t io_bytes) {
   FwdPlan pl{};
   pl.segment_len = split_len(a.B, a.L, a.D, a.N, io_bytes);
   pl.segments = pl.segment_len ? (a.L + pl.segment_len - 1) / pl.segment_len : 1;
+  pl.first_pass_len = piece_len(a.B, a.L, a.D, a.N, io_bytes);
   if (N == 16 && pl.segment_len == 0 && a.L <= ws_max_rows(a.D, io_bytes)) {
     // 16 states, no sequence split, and every row of a (B,L,D) array within
     // 32-bit offsets: the wave-specialised kernel, also for the options
@@ -1096,10 +1141,13 @@ hipError_t noalloc_scratch(void **ptr) {
 }
 
 int64_t fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int io_dtype) {
-  const int64_t len = split_len(B, L, D, N, io_dtype == 0 ? 4 : 2);
+  const int64_t io_bytes = io_dtype == 0 ? 4 : 2;
+  const int64_t len = split_len(B, L, D, N, io_bytes);
   if (len == 0) return 0;
   const int64_t nseg = (L + len - 1) / len;
-  return (2 * B * nseg * D * N + B * nseg * D) * 4;
+  const int64_t nrow = (L + piece_len(B, L, D, N, io_bytes) - 1) / piece_len(B, L, D, N, io_bytes);
+  // end states and step-size sums of the first pass's pieces; segment start states
+  return (B * nrow * D * N + B * nrow * D + B * nseg * D * N) * 4;
 }
 
 hipError_t launch_fwd(const FwdArgs &a, int io_dtype, hipStream_t s) {

@@ -132,6 +132,7 @@ int ssm_scan_fwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate
   plan->tile_channels = p.tile_channels;
   plan->segments = p.segments;
   plan->segment_len = p.segment_len;
+  plan->first_pass_len = p.first_pass_len;
   return SSM_OK;
 }
 

@@ -52,7 +52,8 @@ def scan_fwd_plan(batch, seqlen, dim, dstate, dtype=torch.float32, zoh=False, re
                   per_token=False, accumulate=False, conv_width=0) -> dict:
     """How the forward would run these sizes on the current device (a host
     query, nothing is launched): ``kernel`` ("all-purpose" or
-    "wave-specialised"), ``tile_channels``, ``segments`` and ``segment_len``."""
+    "wave-specialised"), ``tile_channels``, ``segments``, ``segment_len`` and
+    ``first_pass_len`` (steps per piece of a split's first pass)."""
     if dtype not in _IO:
         raise TypeError(f"io dtype must be float32 or bfloat16, got {dtype}")
     lib = _lib.load()
@@ -64,7 +65,7 @@ def scan_fwd_plan(batch, seqlen, dim, dstate, dtype=torch.float32, zoh=False, re
                                      plan))
     return {"kernel": ("all-purpose", "wave-specialised")[plan.kernel],
             "tile_channels": int(plan.tile_channels), "segments": int(plan.segments),
-            "segment_len": int(plan.segment_len)}
+            "segment_len": int(plan.segment_len), "first_pass_len": int(plan.first_pass_len)}
 
 
 def _flags(delta, u, zoh=False, reverse=False, accumulate=False):

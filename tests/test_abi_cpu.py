@@ -73,7 +73,7 @@ def test_binding_signatures_match_the_header(lib):
 
 
 def test_version_and_queries(lib):
-    assert lib.ssm_abi_version() == 3
+    assert lib.ssm_abi_version() == 4
     T = lib.ssm_scan_chunk_len()
     assert T >= 16 and T & (T - 1) == 0
     assert lib.ssm_scan_chunk_states_bytes(2, T * 3 + 1, 64, 16) == 2 * 4 * 64 * 16 * 4
@@ -223,11 +223,14 @@ def test_fwd_plan_query(lib, sizes, io, flags, conv, expect):
     plan = _lib.FwdPlan()
     assert lib.ssm_scan_fwd_plan(*sizes, io, flags, conv, ctypes.byref(plan)) == OK
     assert (plan.kernel, plan.tile_channels, plan.segments) == expect
-    assert (plan.segment_len == 0) == (plan.segments == 1)
+    assert (plan.segment_len == 0) == (plan.segments == 1) == (plan.first_pass_len == 0)
     if plan.segments > 1:
         B, L, D, N = sizes
         assert plan.segments == -(-L // plan.segment_len)
-        assert lib.ssm_scan_fwd_workspace_bytes(*sizes, io) == 4 * B * plan.segments * D * (2 * N + 1)
+        # the first pass cuts every segment into whole pieces of whole chunks
+        assert plan.segment_len % plan.first_pass_len == 0 and plan.first_pass_len % 32 == 0
+        rows = -(-L // plan.first_pass_len)  # pieces over the whole length
+        assert lib.ssm_scan_fwd_workspace_bytes(*sizes, io) == 4 * B * D * (rows * (N + 1) + plan.segments * N)
 
 
 def test_noalloc_forward_rejects_oversized_scratch(lib):

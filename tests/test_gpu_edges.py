@@ -70,7 +70,7 @@ def _assert_plan(ssm, p, tile, zoh=False, reverse=False, conv=0):
     plan = ssm.scan_fwd_plan(Bsz, L, D, p["A"].shape[1], p["B"].dtype, zoh=zoh, reverse=reverse,
                              per_token=p["delta"].dim() == 2, conv_width=conv)
     assert plan == {"kernel": "wave-specialised", "tile_channels": tile, "segments": 1,
-                    "segment_len": 0}, plan
+                    "segment_len": 0, "first_pass_len": 0}, plan
 
 
 @pytest.mark.parametrize("opts", [dict(), dict(zoh=True), dict(reverse=True, tok=True)],

@@ -72,6 +72,19 @@ def test_fwd_options_sequence_split(ssm, B, L, D, N, dtype, zoh):
     _check_fwd(ssm, p, TOL[dtype], zoh=zoh, reverse=True)
 
 
+@pytest.mark.parametrize("opts", [dict(), dict(zoh=True, reverse=True, tok=True)], ids=["plain", "all"])
+@pytest.mark.parametrize("B,L,D,dtype", [(1, 24576, 24, torch.float32), (2, 12288, 16, torch.bfloat16)])
+def test_fwd_split_first_pass_in_pieces(ssm, B, L, D, dtype, opts):
+    """A split whose first pass leaves most CUs idle cuts each segment into
+    pieces for that pass (ssm_scan_fwd_plan reports their length); the start
+    states of the segments are the composition of the pieces' maps."""
+    p = _with_opts(_problem(B, L, D, 16, dtype, seed=L % 101, h0=True, generic_A=True), opts.get("tok"))
+    plan = ssm.scan_fwd_plan(B, L, D, 16, dtype, zoh=opts.get("zoh", False),
+                             reverse=opts.get("reverse", False), per_token=opts.get("tok", False))
+    assert plan["segments"] > 1 and plan["segment_len"] // plan["first_pass_len"] >= 2, plan
+    _check_fwd(ssm, p, TOL[dtype], opts.get("zoh", False), opts.get("reverse", False))
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_fwd_accumulate_and_bidirectional(ssm, dtype):
     p = _problem(2, 150, 72, 16, dtype, seed=31)

@@ -233,6 +233,22 @@ def test_fwd_plan_query(lib, sizes, io, flags, conv, expect):
         assert lib.ssm_scan_fwd_workspace_bytes(*sizes, io) == 4 * B * D * (rows * (N + 1) + plan.segments * N)
 
 
+@pytest.mark.parametrize("sizes,io,segment_len,first_pass_len", [
+    ((1, 32768, 5120, 16), 1, 10944, 3648),       # 32K context: 2 x 80 first-pass tiles, cut in 3
+    ((1, 1 << 20, 1024, 16), 1, 16384, 16384),    # million-length: the first pass fills 4 rounds
+    ((1, 24576, 24, 16), 0, 4096, 2048),          # one tile: pieces no shorter than 2048 steps
+    ((1, 13868, 16, 16), 1, 4640, 4640),          # no whole-chunk piece of 2048 steps or more
+    ((2, 9000, 24, 8), 0, 4512, 4512),            # other state counts: no pieces
+])
+def test_fwd_plan_first_pass_pieces(lib, sizes, io, segment_len, first_pass_len):
+    """How a split's first pass is cut: pieces where whole rounds of them over
+    256 compute units save at least 5% of its time, none elsewhere."""
+    from selective_state_space_10_amd import _lib
+    plan = _lib.FwdPlan()
+    assert lib.ssm_scan_fwd_plan(*sizes, io, 0, 0, ctypes.byref(plan)) == OK
+    assert (plan.segment_len, plan.first_pass_len) == (segment_len, first_pass_len)
+
+
 def test_noalloc_forward_rejects_oversized_scratch(lib):
     """The allocation-free forward holds a fixed scratch of 16 MiB: sizes whose
     forward workspace is larger are refused before anything is enqueued (and

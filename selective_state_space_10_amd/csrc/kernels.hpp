@@ -33,8 +33,10 @@ struct FwdArgs {
   void *workspace;
   int64_t workspace_bytes;
   // sequence split (set by the launcher): segment length in steps (0 = one
-  // segment), per-segment local end states, summed step sizes, and the true
-  // states entering each segment; all (B, nseg, D[, N]) fp32 in the workspace
+  // segment; the first pass gets the length of its pieces), the local end
+  // states and summed step sizes of the first pass's segments or pieces
+  // ((B, rows, D, N) and (B, rows, D), rows = ceil(L / that length)), and the
+  // true states entering each segment ((B, nseg, D, N)); fp32, in the workspace
   int64_t seg_len;
   float *seg_hloc, *seg_dsum, *seg_state;
   // causal depthwise convolution + SiLU producing u from x (conv_k = 0: u is given)

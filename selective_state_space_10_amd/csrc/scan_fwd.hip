@@ -44,8 +44,9 @@ namespace ssm {
 constexpr int64_t kXcds = 8;
 
 // MODE 0: full forward (y, chunk states, final state).  MODE 1: first phase of
-// a sequence split: the segment's end state from a zero start, and the sum of
-// its step sizes (no y).  blockIdx.z is the segment.
+// a sequence split: the segment's (or piece's, as the launcher sets seg_len)
+// end state from a zero start, and the sum of its step sizes (no y).
+// blockIdx.z is the segment.
 // ZOH: exact zero-order-hold input term expm1(dt A)/A * B * u (reading guide,
 // "Yöntem", discretisation of B) instead of dt * B * u.  FLAGS: the other
 // options (reverse direction, one step size per token, accumulate into y) are
@@ -359,8 +360,8 @@ __global__ void __launch_bounds__(64 * N * CPW / (64 * NPL)) fwd_kernel(FwdArgs 
 // FLAGS also the reverse direction, one step size per token and accumulation
 // into y, with ZOH the exact zero-order hold, with CONV u built by the fused
 // causal convolution and SiLU from x (memory order).  MODE 1 is the first pass
-// of a sequence split: each segment's end state from a zero start and its sum
-// of step sizes, no output.
+// of a sequence split: each segment's (or piece's) end state from a zero start
+// and its sum of step sizes, no output.
 // The recurrence waves only run the recurrence, two states per lane.  The
 // service waves (one per 16 channels) do everything else for the same tile:
 // global loads a few sub-chunks ahead, the step-size prologue and B/C staging

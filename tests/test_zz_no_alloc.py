@@ -70,6 +70,14 @@ def test_noalloc_forward_matches_the_workspace_forward(lib):
     _run(lib, 1, 9000, 16, 16, torch.bfloat16, 2, seed=2)  # smaller, reverse direction
 
 
+def test_noalloc_forward_with_first_pass_pieces(lib):
+    """Splits whose first pass runs in pieces (the pieces' end states and the
+    segments' start states share the static scratch): 6 segments of 2 pieces,
+    then a smaller one of 3 segments of 2 pieces in reverse."""
+    _run(lib, 1, 24576, 24, 16, torch.float32, 0, seed=5)
+    _run(lib, 1, 12288, 16, 16, torch.bfloat16, 2, seed=6)
+
+
 def test_noalloc_forward_without_split_and_other_states(lib):
     """Sizes that need no workspace, and a split with 4 states (the
     all-purpose kernel's split)."""

@@ -1,0 +1,151 @@
+"""Full-size parity of the benchmark's option workloads, each in the launch
+configuration `bench.py` times (same shapes, same seeded inputs, same entry
+points), against the fp64 oracle on sampled channels:
+
+- the Mamba-370m forward with one step size per token (the first channel's
+  raw draw as a (batch, length) delta) and bidirectional (two launches, the
+  reverse one accumulating into y);
+- the decode step with the exact zero-order hold, all 64 steps;
+- the Mamba-370m backward with the exact hold and with the fused width-4
+  convolution.  The cotangent is zero outside the sampled channels, so dB and
+  dC (sums over channels) are sums over those channels, which the oracle
+  computes, and every gradient of the other channels must be exactly zero.
+
+Bounds: max|gpu - oracle| / max|oracle| <= 1e-4 (fp32 inputs), 2e-2 (bf16).
+"""
+from __future__ import annotations
+
+import pytest
+import torch
+
+from oracle import oracle_c
+from tests.helpers import nmax_err
+from tests.test_gpu_parity import TOL, _decode_check, _oracle_kwargs, _slice_channels
+from workloads import WORKLOADS, conv_inputs, cotangent, decode_inputs, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+# channels at both ends of a 64-channel tile, both lane parities, a middle
+# tile and the last channel of the Mamba-370m layer (2048 channels)
+_SEL_370M = torch.tensor([0, 1, 62, 63, 64, 777, 1030, 1500, 2046, 2047])
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_10_amd as m
+    m.load()
+    return m
+
+
+def _mask(dim, sel):
+    m = torch.zeros(dim, dtype=torch.bool)
+    m[sel] = True
+    return m.cuda()
+
+
+def test_fwd_token_delta_workload1_full_size(ssm):
+    """One raw step size per token at the Mamba-370m shape (fp32, y and the
+    final state), on sampled channels."""
+    print("full-size forward, one step size per token, 8 x 2048 x 2048", flush=True)
+    w = WORKLOADS[1]
+    p = workload_inputs(1, device="cuda")
+    p["delta"] = p["delta"][:, :, 0].contiguous()
+    y, hf, _ = ssm.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                            p["delta_bias"], True, None, return_final_state=True)
+    torch.cuda.synchronize()
+    sc = _SEL_370M.cuda()
+    ps = _slice_channels(dict(p, delta=None), sc)
+    ps["delta"] = p["delta"].cpu()  # (batch, length): shared by every channel
+    yo, hfo, _ = oracle_c.scan_fwd(**_oracle_kwargs(ps))
+    assert nmax_err(y[:, :, sc], yo) <= TOL[w.io_dtype]
+    assert nmax_err(hf[:, sc], hfo) <= TOL[w.io_dtype]
+
+
+def test_bidirectional_workload1_full_size(ssm):
+    """Both directions summed at the Mamba-370m shape (fp32): the forward
+    launch with the skip term, the reverse launch adding its gated state
+    contribution into y."""
+    print("full-size bidirectional forward, 8 x 2048 x 2048", flush=True)
+    w = WORKLOADS[1]
+    p = workload_inputs(1, device="cuda")
+    y = ssm.bidirectional_scan(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                               p["delta_bias"], True)
+    torch.cuda.synchronize()
+    sc = _SEL_370M.cuda()
+    ok = _oracle_kwargs(_slice_channels(p, sc))
+    yf, _, _ = oracle_c.scan_fwd(**ok)
+    yr, _, _ = oracle_c.scan_fwd(**dict(ok, D=None), reverse=True)
+    assert nmax_err(y[:, :, sc], yf + yr) <= TOL[w.io_dtype]
+
+
+def test_decode_zoh_workload3_full_size(ssm):
+    """64 decode steps with the exact hold on the (256, 5120, 16) state, on
+    sampled channels."""
+    print("full-size decode with the exact hold, 256 x 5120 x 16, 64 steps", flush=True)
+    w = WORKLOADS[3]
+    d = decode_inputs(w.batch, w.dim, w.dstate, w.steps, w.io_dtype, seed=3)
+    sel = torch.tensor([0, 1, 2, 3, 2559, 2560, 4093, 5118, 5119])
+    _decode_check(ssm, d, w.steps, TOL[w.io_dtype], sel=sel, zoh=True)
+
+
+def test_bwd_zoh_workload1_shape_full_size(ssm):
+    """Backward with the exact hold at the Mamba-370m shape (fp32)."""
+    print("full-size backward with the exact hold, 8 x 2048 x 2048", flush=True)
+    w = WORKLOADS[1]
+    p = workload_inputs(1, device="cuda")
+    y, _, cs = ssm.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                            p["delta_bias"], True, None, save_chunk_states=True, zoh=True)
+    mg = _mask(w.dim, _SEL_370M)
+    dy = cotangent(y, 1)
+    dy[:, :, ~mg] = 0
+    del y
+    gr = ssm.scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                      p["delta_bias"], True, None, cs, dy, zoh=True)
+    torch.cuda.synchronize()
+    sc = _SEL_370M.cuda()
+    ps = _slice_channels(dict(p, dy=dy), sc)
+    go = oracle_c.scan_bwd(**_oracle_kwargs(ps), dy=ps["dy"], zoh=True)
+    tol = TOL[w.io_dtype]
+    for k in ("du", "ddelta", "dz"):
+        assert nmax_err(gr[k][:, :, sc], go[k]) <= tol, k
+        assert int(torch.count_nonzero(gr[k][:, :, ~mg])) == 0, k
+    for k in ("dB", "dC"):
+        assert nmax_err(gr[k], go[k]) <= tol, k
+    for k in ("dA", "dD", "ddelta_bias"):
+        assert nmax_err(gr[k][sc], go[k]) <= tol, k
+        assert int(torch.count_nonzero(gr[k][~mg])) == 0, k
+
+
+def test_bwd_conv_workload1_shape_full_size(ssm):
+    """Backward of the fused width-4 convolution and the scan at the
+    Mamba-370m shape (fp32), with the taps the benchmark draws."""
+    print("full-size backward with the fused convolution, 8 x 2048 x 2048", flush=True)
+    w = WORKLOADS[1]
+    p = workload_inputs(1, device="cuda")
+    cw, cb = conv_inputs(w.dim, 4, seed=1, device="cuda")
+    y, _, cs = ssm.scan_fwd_conv(p["u"], cw, cb, p["delta"], p["A"], p["B"], p["C"], p["D"],
+                                 p["z"], p["delta_bias"], True, None, save_chunk_states=True)
+    mg = _mask(w.dim, _SEL_370M)
+    dy = cotangent(y, 1)
+    dy[:, :, ~mg] = 0
+    del y
+    gr = ssm.scan_bwd_conv(p["u"], cw, cb, p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                           p["delta_bias"], True, None, cs, dy)
+    torch.cuda.synchronize()
+    sc = _SEL_370M.cuda()
+    ps = dict(x=p["u"][:, :, sc].cpu(), conv_w=cw[sc].cpu(), conv_b=cb[sc].cpu(),
+              delta=p["delta"][:, :, sc].cpu(), A=p["A"][sc].cpu(), B=p["B"].cpu(),
+              C=p["C"].cpu(), D=p["D"][sc].cpu(), z=p["z"][:, :, sc].cpu(),
+              delta_bias=p["delta_bias"][sc].cpu(), delta_softplus=True, h0=None)
+    go = oracle_c.scan_bwd_conv(**ps, dy=dy[:, :, sc].cpu())
+    tol = TOL[w.io_dtype]
+    for k in ("dx", "ddelta", "dz"):
+        assert nmax_err(gr[k][:, :, sc], go[k]) <= tol, k
+        assert int(torch.count_nonzero(gr[k][:, :, ~mg])) == 0, k
+    for k in ("dB", "dC"):
+        assert nmax_err(gr[k], go[k]) <= tol, k
+    for k in ("dconv_w", "dconv_b", "dA", "dD", "ddelta_bias"):
+        assert nmax_err(gr[k][sc], go[k]) <= tol, k
+        assert int(torch.count_nonzero(gr[k][~mg])) == 0, k

@@ -239,7 +239,7 @@ def test_fwd_deterministic_and_stream(ssm):
 # ---------------------------------------------------------------- decode
 
 
-def _decode_check(ssm, d, steps, tol, sel=None):
+def _decode_check(ssm, d, steps, tol, sel=None, zoh=False):
     dg = _to(d, "cuda")
     state = dg["state"].clone()
     ys = []
@@ -247,7 +247,7 @@ def _decode_check(ssm, d, steps, tol, sel=None):
         ys.append(ssm.state_update(state, dg["u"][t], dg["delta"][t], dg["A"], dg["B"][t],
                                    dg["C"][t], dg.get("D"), None if dg.get("z") is None
                                    else dg["z"][t], dg.get("delta_bias"),
-                                   d.get("delta_softplus", True)))
+                                   d.get("delta_softplus", True), zoh=zoh))
     torch.cuda.synchronize()
     yg = torch.stack(ys)
     if sel is None:
@@ -260,7 +260,7 @@ def _decode_check(ssm, d, steps, tol, sel=None):
             None if d.get("D") is None else d["D"][sel],
             None if d.get("z") is None else d["z"][t][:, sel],
             None if d.get("delta_bias") is None else d["delta_bias"][sel],
-            d.get("delta_softplus", True))
+            d.get("delta_softplus", True), zoh=zoh)
         yo.append(yt)
     assert nmax_err(yg[:, :, sel.cuda()], np.stack(yo)) <= tol
     assert nmax_err(state[:, sel.cuda()], so) <= tol

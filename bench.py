@@ -15,7 +15,7 @@ line (rank 0).
 the same with the fused width-4 convolution (mamba-2.8b-layer-fwd-conv4),
 the 32K-context forward at the 2.8b width (mamba-2.8b-32k-fwd),
 decode-state-update, million-length-fwd, million-length-bwd,
-mamba-370m-layer-bwd, the 370m forward with the exact zero-order hold, with one
+mamba-370m-layer-bwd, the backward at the 2.8b shape (mamba-2.8b-layer-bwd), the 370m forward with the exact zero-order hold, with one
 step size per token, bidirectional or with the fused convolution, the 370m
 backward with the exact hold or the fused convolution, and the decode step with
 the exact hold); their lines use the same keys and are for reference, the
@@ -48,7 +48,7 @@ WORKLOAD_NAMES = ["mamba-370m-layer-fwd", "mamba-2.8b-layer-fwd", "decode-state-
                   "mamba-370m-layer-fwd-zoh", "mamba-370m-layer-fwd-token-delta",
                   "mamba-370m-layer-bidirectional", "decode-state-update-zoh",
                   "mamba-370m-layer-fwd-conv4", "mamba-370m-layer-bwd-conv4", "mamba-370m-layer-bwd-zoh",
-                  "mamba-2.8b-32k-fwd", "mamba-2.8b-layer-fwd-conv4"]
+                  "mamba-2.8b-32k-fwd", "mamba-2.8b-layer-fwd-conv4", "mamba-2.8b-layer-bwd"]
 METRIC = "selective-scan fwd tokens·channels/s and HBM GB/s (% of peak), Mamba-370m shape"
 # The only throughput figure the source pages give for the method is relative and
 # names no hardware, precision or workload: context beside the kernel's rate, not
@@ -735,6 +735,8 @@ def main():
         line = bench_fwd(args, 2, wl, conv=4)
     elif wl == "mamba-370m-layer-bwd-conv4":
         line = bench_bwd(args, 1, wl, conv=4)
+    elif wl == "mamba-2.8b-layer-bwd":
+        line = bench_bwd(args, 2, wl)
     elif wl == "mamba-370m-layer-bwd-zoh":
         line = bench_bwd(args, 1, wl, zoh=True)
     else:

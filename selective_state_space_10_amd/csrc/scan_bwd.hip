@@ -88,9 +88,12 @@ inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 // smallest that gives at least two rounds is taken (later workgroups fill in
 // behind the first round's slowest ones: 22.1 ms against 23.5 ms for 32
 // against 16 segments at the million-length shape), else the smallest.
-// Segments are multiples of 256 steps, at least kMinSeg long.  Depends on
-// sizes only.
-constexpr int64_t kMinSeg = 2048;
+// Segments are multiples of 256 steps, at least kMinSeg long: segments this
+// short let shapes just above one round fill whole rounds (measured on MI355X:
+// the Mamba-2.8b shape, 4 x 4096 x 5120 bf16, 1.97 ms with 2 segments of 2048
+// steps against 1.67 ms with 4 of 1024; 10 x 2048 x 2048 fp32 1.04 ms unsplit
+// against 0.81 ms with 4 of 512).  Depends on sizes only.
+constexpr int64_t kMinSeg = 512;
 constexpr int64_t kCUs = 256;
 constexpr double kMode1 = 0.23;
 

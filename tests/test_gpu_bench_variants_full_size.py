@@ -7,9 +7,10 @@ points), against the fp64 oracle on sampled channels:
   reverse one accumulating into y);
 - the decode step with the exact zero-order hold, all 64 steps;
 - the Mamba-370m backward with the exact hold and with the fused width-4
-  convolution.  The cotangent is zero outside the sampled channels, so dB and
-  dC (sums over channels) are sums over those channels, which the oracle
-  computes, and every gradient of the other channels must be exactly zero.
+  convolution, and the Mamba-2.8b backward (a split sequence).  The
+  cotangent is zero outside the sampled channels, so dB and dC (sums over
+  channels) are sums over those channels, which the oracle computes, and
+  every gradient of the other channels must be exactly zero.
 
 Bounds: max|gpu - oracle| / max|oracle| <= 1e-4 (fp32 inputs), 2e-2 (bf16).
 """
@@ -147,5 +148,37 @@ def test_bwd_conv_workload1_shape_full_size(ssm):
     for k in ("dB", "dC"):
         assert nmax_err(gr[k], go[k]) <= tol, k
     for k in ("dconv_w", "dconv_b", "dA", "dD", "ddelta_bias"):
+        assert nmax_err(gr[k][sc], go[k]) <= tol, k
+        assert int(torch.count_nonzero(gr[k][~mg])) == 0, k
+
+
+def test_bwd_workload2_full_size(ssm):
+    """Backward at the Mamba-2.8b layer shape (4 x 4096 x 5120, bf16) as the
+    benchmark runs it: 320 channel tiles, so the sequence is split into four
+    segments of 1024 steps (first pass, composition of the carries, full
+    pass), on sampled channels at both ends of 64-channel tiles."""
+    print("full-size backward, 4 x 4096 x 5120 bf16 (split sequence)", flush=True)
+    w = WORKLOADS[2]
+    p = workload_inputs(2, device="cuda")
+    y, _, cs = ssm.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                            p["delta_bias"], True, None, save_chunk_states=True)
+    sel = torch.tensor([0, 1, 63, 64, 1999, 2048, 2559, 2560, 4095, 5118, 5119])
+    mg = _mask(w.dim, sel)
+    dy = cotangent(y, 2)
+    dy[:, :, ~mg] = 0
+    del y
+    gr = ssm.scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                      p["delta_bias"], True, None, cs, dy)
+    torch.cuda.synchronize()
+    sc = sel.cuda()
+    ps = _slice_channels(dict(p, dy=dy), sc)
+    go = oracle_c.scan_bwd(**_oracle_kwargs(ps), dy=ps["dy"])
+    tol = TOL[w.io_dtype]
+    for k in ("du", "ddelta", "dz"):
+        assert nmax_err(gr[k][:, :, sc], go[k]) <= tol, k
+        assert int(torch.count_nonzero(gr[k][:, :, ~mg])) == 0, k
+    for k in ("dB", "dC"):
+        assert nmax_err(gr[k], go[k]) <= tol, k
+    for k in ("dA", "dD", "ddelta_bias"):
         assert nmax_err(gr[k][sc], go[k]) <= tol, k
         assert int(torch.count_nonzero(gr[k][~mg])) == 0, k

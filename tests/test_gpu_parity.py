@@ -380,7 +380,10 @@ def test_bwd_options(ssm, opts):
 
 @pytest.mark.parametrize("B,L,D,N,dtype", [
     (1, 5000, 16, 16, torch.float32), (2, 9000, 24, 8, torch.float32),
-    (1, 6000, 8, 16, torch.bfloat16), (1, 4500, 8, 1, torch.float32)])
+    (1, 6000, 8, 16, torch.bfloat16), (1, 4500, 8, 1, torch.float32),
+    # segments of the shortest length, 512 steps: 16 of them (composed by the
+    # wave-wide scan) and 8 (composed by the per-thread fold)
+    (1, 8192, 8, 16, torch.float32), (1, 4096, 16, 16, torch.bfloat16)])
 def test_bwd_sequence_split(ssm, B, L, D, N, dtype):
     """Few channels and a long sequence: the backward splits the sequence into
     segments (local adjoint carries, their composition from the right, then the

@@ -15,7 +15,8 @@ line (rank 0).
 the same with the fused width-4 convolution (mamba-2.8b-layer-fwd-conv4),
 the 32K-context forward at the 2.8b width (mamba-2.8b-32k-fwd),
 decode-state-update, million-length-fwd, million-length-bwd,
-mamba-370m-layer-bwd, the backward at the 2.8b shape (mamba-2.8b-layer-bwd), the 370m forward with the exact zero-order hold, with one
+mamba-370m-layer-bwd, the backward at the 2.8b shape (mamba-2.8b-layer-bwd),
+the 370m forward with the exact zero-order hold, with one
 step size per token, bidirectional or with the fused convolution, the 370m
 backward with the exact hold or the fused convolution, and the decode step with
 the exact hold); their lines use the same keys and are for reference, the
